@@ -1,0 +1,222 @@
+/*
+ * rfattn.h -- C ABI of librfattn: rolling-window DiT attention with 3D-RoPE
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the problem statement of the source pages (the
+ * Amazon Science post "A kernel-centric path to real-time video generation
+ * on Trainium" and its digests):
+ *   - video RoPE rotates over three axes, time, height and width
+ *     ("Amazon and Reactor tune Trainium for real-time video generation",
+ *     section "Three problems for generic compilers");
+ *   - every layer reads and writes a rolling KV cache, frames are generated
+ *     and evicted in a sliding window, and attention lengths vary between
+ *     passes (same section);
+ *   - 23,400 query tokens attend to 32,760 context tokens over 12 heads
+ *     (ai4snews digest, second paragraph; brifing.si "Optimizing Real-Time
+ *     Video Generation on Trainium Chips", section 4);
+ *   - the denoise pass and the lighter cache-update pass run batched
+ *     together ("Optimizing Real-Time Video Generation on Trainium Chips",
+ *     section 8; vibeleaderboard digest, key takeaways);
+ *   - transposes happen inside the kernels, never as passes of their own
+ *     (vibeleaderboard digest, key takeaways; ai4snews, first paragraph).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are bf16 (raw 16-bit patterns) in device memory that the
+ *     CALLER owns.  The library allocates device memory only in rf_create
+ *     (the RoPE tables) and frees it in rf_destroy.
+ *   - Calls are asynchronous and stream-ordered: work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream)
+ *     and the call returns without synchronising.
+ *   - Validation happens on the host before anything is enqueued.  On any
+ *     error nothing is enqueued and no descriptor is modified.  RF_ERR_HIP
+ *     reports a failed launch; rf_last_error() gives the detail.
+ *   - "Token-major" means [tokens][ld] elements, heads contiguous inside a
+ *     row: element (token i, head h, dim d) is at i*ld + h*head_dim + d.
+ *     ld is in elements, >= n_heads*head_dim and a multiple of 8; every
+ *     pointer is 16-byte aligned.
+ *   - Token positions: token i of a block whose first frame is t0 is at
+ *     (frame t0 + i/N, row (i%N)/grid_w, column i%grid_w), N = grid_h*grid_w.
+ *     Frames are absolute latent frame indices in 0..max_frame-1.
+ */
+#ifndef RFATTN_H
+#define RFATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RF_OK = 0,
+  RF_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  RF_ERR_ALIGN = 2,       /* pointer not 16-byte aligned or ld not a multiple of 8 */
+  RF_ERR_SHAPE = 3,       /* unsupported geometry or inconsistent sizes          */
+  RF_ERR_RANGE = 4,       /* frames outside the ring window or the RoPE tables   */
+  RF_ERR_UNSUPPORTED = 5, /* current device is not gfx950                        */
+  RF_ERR_HIP = 6          /* HIP runtime error (allocation, copy or launch)      */
+} rf_status;
+
+/* Model geometry, fixed for the lifetime of a context. */
+typedef struct {
+  int32_t grid_h, grid_w;  /* latent frame grid; N = grid_h*grid_w tokens per frame,
+                              N must be a multiple of 8                             */
+  int32_t n_heads;         /* H >= 1 (query heads == key/value heads)               */
+  int32_t head_dim;        /* D; this library supports 128                          */
+  int32_t rope_pairs[3];   /* rotation pairs on the time, row and column axes;
+                              sum == D/2.  Pair p rotates dims (2p, 2p+1); pairs
+                              0..P_t-1 use the frame index, the next P_h the row,
+                              the last P_w the column                               */
+  double rope_base;        /* frequency base b: pair j of an axis with P pairs
+                              turns by pos * b^(-j/P) radians                       */
+  int64_t max_frame;       /* frame indices 0..max_frame-1 are supported            */
+} rf_geom;
+
+/* Opaque context: the geometry plus the device-resident cos/sin tables (each
+ * float64 libm cos/sin of pos*b^(-j/P), rounded to float32).  Immutable after
+ * creation; one context may be used from several threads and streams. */
+typedef struct rf_ctx rf_ctx;
+
+/* Validate `g`, check that the current HIP device is gfx950, and upload the
+ * RoPE tables.  This is the library's only allocation.  *out is set only on
+ * RF_OK.  Synchronous. */
+rf_status rf_create(const rf_geom* g, rf_ctx** out);
+
+/* Free a context (NULL is ignored).  The caller must first make sure no work
+ * that uses it is still queued. */
+void rf_destroy(rf_ctx* ctx);
+
+/* Human-readable name of a status code (static storage). */
+const char* rf_status_string(rf_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* rf_last_error(void);
+
+/*
+ * rf_rope3d_apply -- 3D rotary embedding of a token-major bf16 tensor.
+ *
+ * Source: RoPE over time, height and width ("Amazon and Reactor tune
+ * Trainium for real-time video generation", section "Three problems for
+ * generic compilers"; the pages report a hand-written kernel for it,
+ * section "Results with the Neuron Kernel Interface").
+ *
+ * x: [n_tokens][x_ld] bf16, heads contiguous; y: [n_tokens][y_ld].  y may
+ * equal x with y_ld == x_ld (in place); other overlaps are not allowed.
+ * Token i sits at (t0 + i/N, (i%N)/grid_w, i%grid_w).  For every pair p:
+ *   y[2p]   = bf16_rne( fl64( x[2p]*c - x[2p+1]*s ) )
+ *   y[2p+1] = bf16_rne( fl64( x[2p]*s + x[2p+1]*c ) )
+ * with c, s the float32 table entries; the products are exact in float64,
+ * so the result is unique and reproducible bit for bit.
+ * n_tokens == 0 is a no-op.  Errors: RF_ERR_NULL, RF_ERR_ALIGN,
+ * RF_ERR_SHAPE (ld too small, n_tokens < 0), RF_ERR_RANGE (t0 < 0 or the
+ * last token's frame >= max_frame).
+ */
+rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* y,
+                          int64_t y_ld, int64_t t0, int64_t n_tokens, void* stream);
+
+/*
+ * Ring-buffer KV cache of `capacity` frame slots.  Frame t lives in slot
+ * t % capacity.  Valid frames: first .. first+count-1 (count <= capacity).
+ *   k: bf16 [capacity][H][N][D] -- keys, already rotated by 3D-RoPE at their
+ *      own positions, head-major inside a slot (rows of D contiguous);
+ *   v: bf16 [capacity][H][D][N] -- values, transposed inside a slot so that a
+ *      head's keys are contiguous for each dim.
+ * The caller allocates both (capacity*H*N*D*2 bytes each, 16-byte aligned)
+ * and zero-fills or otherwise initialises them; a new cache has count == 0.
+ * The library reads and writes the descriptor only inside rf_kvcache_roll.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t capacity; /* W >= 1 */
+  int32_t count;    /* 0..capacity */
+  int64_t first;    /* oldest valid frame (any value while count == 0) */
+} rf_kvcache;
+
+/*
+ * rf_kvcache_roll -- write n_frames new frames t0..t0+n_frames-1 into the
+ * ring in one pass: keys are rotated by 3D-RoPE (bit-exact, as
+ * rf_rope3d_apply) and stored head-major, values are stored transposed; no
+ * separate transpose or copy pass.  Frames already in the window are
+ * overwritten in place; later frames are appended, and appending to a full
+ * ring evicts the oldest frame (its slot is the one written).  Other slots
+ * are left untouched.
+ *
+ * Source: the rolling KV cache that every layer reads and writes, frames
+ * generated and evicted in a sliding window ("Amazon and Reactor tune
+ * Trainium for real-time video generation", section "Three problems for
+ * generic compilers"); the pages report a hand-written cache-copy kernel
+ * (section "Results with the Neuron Kernel Interface").
+ *
+ * k_new, v_new: token-major [n_frames*N][ld] bf16, un-rotated.
+ * Requires 1 <= n_frames <= capacity and, unless the ring is empty,
+ * first <= t0 <= first+count (an empty ring starts its window at t0).
+ * On RF_OK, *c's first/count are updated on the host after the kernel is
+ * enqueued; on error *c is unchanged.  The caller serialises calls that
+ * share a descriptor.
+ */
+rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, int64_t k_ld,
+                          const void* v_new, int64_t v_ld, int64_t t0, int32_t n_frames,
+                          void* stream);
+
+/*
+ * rf_kvcache_plan_roll -- host-only: validate a roll as rf_kvcache_roll
+ * would and write the descriptor it would leave into *after (first, count;
+ * k, v and capacity copied).  Touches no device.  Lets a caller that keeps
+ * one descriptor per layer advance them in lockstep.
+ */
+rf_status rf_kvcache_plan_roll(const rf_kvcache* c, int64_t t0, int32_t n_frames,
+                               rf_kvcache* after);
+
+/* One group of query tokens and the context frames they attend to. */
+typedef struct {
+  const void* q;      /* token-major [q_frames*N][q_ld] bf16, un-rotated queries  */
+  int64_t q_ld;
+  void* o;            /* token-major [q_frames*N][o_ld] bf16 output              */
+  int64_t o_ld;
+  int64_t q_t0;       /* frame index of q's first token (its RoPE position)       */
+  int32_t q_frames;   /* >= 1                                                     */
+  int32_t ctx_frames; /* >= 1 context frames ctx_t0 .. ctx_t0+ctx_frames-1, all   */
+  int64_t ctx_t0;     /*      inside the ring's valid window                      */
+} rf_attn_segment;
+
+#define RF_MAX_SEGMENTS 8
+
+/*
+ * rf_window_attention -- non-causal multi-head attention of each segment's
+ * query tokens over its context frames in the ring, all segments in ONE
+ * launch (the denoise pass and the cache-update pass batched together).
+ *
+ * Source: the DiT self-attention, 23,400 queries over 32,760 context
+ * tokens in 12 heads, the dominant cost (ai4snews digest, second
+ * paragraph); two passes per window, denoise then cache update, with
+ * attention lengths that vary ("Amazon and Reactor tune Trainium for
+ * real-time video generation", section "Three problems for generic
+ * compilers"); batching the two phases ("Optimizing Real-Time Video
+ * Generation on Trainium Chips", section 8); transposes fused into the
+ * attention kernel (vibeleaderboard digest, key takeaways).
+ *
+ * For each segment, head h and query token i:
+ *   q^ = bf16 RoPE of q_i at its position (as rf_rope3d_apply),
+ *   s_j = scale * <q^, k_j>  over every token j of the context frames
+ *         (k_j as stored: already rotated),
+ *   o_i = sum_j softmax(s)_j v_j, written as bf16 (round to nearest even).
+ * Scores, the softmax and the accumulators are float32; the softmax weights
+ * enter the value product as bf16.  scale == 0 means 1/sqrt(head_dim).
+ * The context length is a runtime argument (whole frames); nothing is
+ * recompiled or reallocated when it changes.
+ *
+ * Errors: RF_ERR_NULL, RF_ERR_ALIGN, RF_ERR_SHAPE (n_segs outside
+ * 1..RF_MAX_SEGMENTS, q_frames/ctx_frames < 1, ld too small), RF_ERR_RANGE
+ * (context not inside first..first+count-1, or query frames beyond the
+ * tables).  Output rows must not overlap between segments.
+ */
+rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c,
+                              const rf_attn_segment* segs, int32_t n_segs, float scale,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RFATTN_H */

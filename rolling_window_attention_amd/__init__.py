@@ -1,0 +1,234 @@
+"""librfattn Python binding: rolling-window DiT attention with 3D-RoPE on MI355X.
+
+A thin ctypes layer over the C ABI in ``include/rfattn.h``.  It only marshals
+arguments -- torch tensors become device pointers and row strides, the current
+torch stream becomes the HIP stream -- and raises ``RfError`` on any non-OK
+status.  Every step of the computation runs in the HIP kernels of
+``librfattn.so``; there is no fallback.  If the library is not built, the
+first call raises.
+
+    ctx = Context()                                   # 30x52 grid, 12 heads of 128
+    cache = KVCache(ctx, capacity=21)                 # ring of 21 frame slots
+    cache.roll(k_new, v_new, t0)                      # RoPE(K) + V^T into the ring
+    window_attention(ctx, cache, [Segment(q, q_t0, o, ctx_t0, ctx_frames), ...])
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librfattn.so")
+
+RF_OK = 0
+STATUS_NAMES = {0: "RF_OK", 1: "RF_ERR_NULL", 2: "RF_ERR_ALIGN", 3: "RF_ERR_SHAPE",
+                4: "RF_ERR_RANGE", 5: "RF_ERR_UNSUPPORTED", 6: "RF_ERR_HIP"}
+MAX_SEGMENTS = 8
+
+# Every entry point include/rfattn.h declares.
+EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
+           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention")
+
+
+class RfError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_pairs", ctypes.c_int32 * 3), ("rope_base", ctypes.c_double),
+                ("max_frame", ctypes.c_int64)]
+
+
+class KVCacheDesc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("first", ctypes.c_int64)]
+
+
+class SegmentDesc(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_ld", ctypes.c_int64), ("o", ctypes.c_void_p),
+                ("o_ld", ctypes.c_int64), ("q_t0", ctypes.c_int64), ("q_frames", ctypes.c_int32),
+                ("ctx_frames", ctypes.c_int32), ("ctx_t0", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librfattn (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc, gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.rf_create.argtypes = [ctypes.POINTER(Geom), ctypes.POINTER(vp)]
+        L.rf_create.restype = i32
+        L.rf_destroy.argtypes = [vp]
+        L.rf_destroy.restype = None
+        L.rf_status_string.argtypes = [i32]
+        L.rf_status_string.restype = ctypes.c_char_p
+        L.rf_last_error.argtypes = []
+        L.rf_last_error.restype = ctypes.c_char_p
+        L.rf_rope3d_apply.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp]
+        L.rf_rope3d_apply.restype = i32
+        L.rf_kvcache_roll.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, i64, i32, vp]
+        L.rf_kvcache_roll.restype = i32
+        L.rf_kvcache_plan_roll.argtypes = [ctypes.POINTER(KVCacheDesc), i64, i32,
+                                           ctypes.POINTER(KVCacheDesc)]
+        L.rf_kvcache_plan_roll.restype = i32
+        L.rf_window_attention.argtypes = [vp, ctypes.POINTER(KVCacheDesc),
+                                          ctypes.POINTER(SegmentDesc), i32, ctypes.c_float, vp]
+        L.rf_window_attention.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != RF_OK:
+        raise RfError(status, lib().rf_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _token_major(t, name, n_heads, head_dim):
+    """Pointer and row stride of a [tokens, H, D] (or [tokens, H*D]) bf16 device tensor."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values")
+    if t.dim() == 3:
+        if t.shape[1:] != (n_heads, head_dim) or t.stride(2) != 1 or t.stride(1) != head_dim:
+            raise ValueError(f"{name} must be [tokens, {n_heads}, {head_dim}] with heads contiguous")
+    elif t.dim() == 2:
+        if t.shape[1] != n_heads * head_dim or t.stride(1) != 1:
+            raise ValueError(f"{name} must be [tokens, {n_heads * head_dim}] with rows contiguous")
+    else:
+        raise ValueError(f"{name} must be token-major [tokens, H, D]")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.shape[0]
+
+
+class Context:
+    """Geometry + device RoPE tables (rf_create / rf_destroy)."""
+
+    def __init__(self, grid_h=30, grid_w=52, n_heads=12, head_dim=128, pairs=(22, 21, 21),
+                 base=10000.0, max_frame=4096):
+        g = Geom(grid_h, grid_w, n_heads, head_dim, (ctypes.c_int32 * 3)(*pairs), base, max_frame)
+        h = ctypes.c_void_p()
+        _check(lib().rf_create(ctypes.byref(g), ctypes.byref(h)))
+        self._h = h
+        self.grid_h, self.grid_w, self.n_heads, self.head_dim = grid_h, grid_w, n_heads, head_dim
+        self.pairs, self.base, self.max_frame = tuple(pairs), base, max_frame
+        self.tokens_per_frame = grid_h * grid_w
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("context is closed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            lib().rf_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def rope3d_apply(self, x, t0, y=None, stream=None):
+        """y = 3D-RoPE(x) for token-major bf16 x whose first token is in frame t0."""
+        if y is None:
+            y = torch.empty_like(x)
+        xp, xld, n = _token_major(x, "x", self.n_heads, self.head_dim)
+        yp, yld, ny = _token_major(y, "y", self.n_heads, self.head_dim)
+        if ny != n:
+            raise ValueError("x and y must have the same number of tokens")
+        _check(lib().rf_rope3d_apply(self.handle, xp, xld, yp, yld, t0, n, _stream(stream)))
+        return y
+
+
+class KVCache:
+    """A ring of `capacity` frame slots: k [W, H, N, D] (rotated), v [W, H, D, N]."""
+
+    def __init__(self, ctx, capacity, device="cuda"):
+        self.ctx = ctx
+        shape_k = (capacity, ctx.n_heads, ctx.tokens_per_frame, ctx.head_dim)
+        shape_v = (capacity, ctx.n_heads, ctx.head_dim, ctx.tokens_per_frame)
+        self.k = torch.zeros(shape_k, dtype=torch.bfloat16, device=device)
+        self.v = torch.zeros(shape_v, dtype=torch.bfloat16, device=device)
+        self.desc = KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(), capacity, 0, 0)
+
+    @property
+    def capacity(self):
+        return self.desc.capacity
+
+    @property
+    def first(self):
+        return self.desc.first
+
+    @property
+    def count(self):
+        return self.desc.count
+
+    def window(self):
+        return list(range(self.desc.first, self.desc.first + self.desc.count))
+
+    def roll(self, k_new, v_new, t0, stream=None):
+        """Write frames t0.. of token-major k_new/v_new ([n*N, H, D]) into the ring."""
+        c = self.ctx
+        kp, kld, nk = _token_major(k_new, "k_new", c.n_heads, c.head_dim)
+        vp, vld, nv = _token_major(v_new, "v_new", c.n_heads, c.head_dim)
+        if nk != nv or nk % c.tokens_per_frame:
+            raise ValueError("k_new and v_new must hold the same whole number of frames")
+        n = nk // c.tokens_per_frame
+        _check(lib().rf_kvcache_roll(c.handle, ctypes.byref(self.desc), kp, kld, vp, vld, t0, n,
+                                     _stream(stream)))
+
+    def plan_roll(self, t0, n_frames):
+        """(first, count) the ring would have after rolling frames t0..t0+n_frames-1."""
+        after = KVCacheDesc()
+        _check(lib().rf_kvcache_plan_roll(ctypes.byref(self.desc), t0, n_frames, ctypes.byref(after)))
+        return after.first, after.count
+
+
+class Segment:
+    """Query tokens q (frames q_t0..) attending to context frames ctx_t0..ctx_t0+ctx_frames-1."""
+
+    def __init__(self, q, q_t0, o, ctx_t0, ctx_frames):
+        self.q, self.q_t0, self.o, self.ctx_t0, self.ctx_frames = q, q_t0, o, ctx_t0, ctx_frames
+
+
+def window_attention(ctx, cache, segments, scale=0.0, stream=None):
+    """All segments in one launch; outputs are written into each segment's o."""
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError(f"1..{MAX_SEGMENTS} segments per launch")
+    arr = (SegmentDesc * len(segments))()
+    for i, s in enumerate(segments):
+        qp, qld, nq = _token_major(s.q, "q", ctx.n_heads, ctx.head_dim)
+        op, old, no = _token_major(s.o, "o", ctx.n_heads, ctx.head_dim)
+        if nq != no or nq % ctx.tokens_per_frame:
+            raise ValueError("q and o must hold the same whole number of frames")
+        arr[i] = SegmentDesc(qp, qld, op, old, s.q_t0, nq // ctx.tokens_per_frame, s.ctx_frames,
+                             s.ctx_t0)
+    _check(lib().rf_window_attention(ctx.handle, ctypes.byref(cache.desc), arr, len(segments),
+                                     scale, _stream(stream)))
+
+
+def plan_roll(capacity, first, count, t0, n_frames):
+    """Host-only ring bookkeeping (rf_kvcache_plan_roll) without any device memory."""
+    d = KVCacheDesc(None, None, capacity, count, first)
+    after = KVCacheDesc()
+    _check(lib().rf_kvcache_plan_roll(ctypes.byref(d), t0, n_frames, ctypes.byref(after)))
+    return after.first, after.count

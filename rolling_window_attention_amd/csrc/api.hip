@@ -1,0 +1,349 @@
+// Host side of librfattn: the C ABI declared in include/rfattn.h.
+//
+// Validation is done here, on the host, before anything is enqueued; the
+// ring-buffer bookkeeping (first/count) lives only in the caller's
+// descriptor; the RoPE tables are built once in float64 with the C library's
+// pow/cos/sin, rounded to float32 and uploaded in rf_create.
+//
+// Sources for the operations: see the comments of include/rfattn.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "rfattn.h"
+
+using namespace rfattn;
+
+struct rf_ctx {
+  rf_geom g;
+  int device;
+  float2* d_tab;  // one allocation: [t table | h table | w table]
+  RopeTables tab;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rf_status fail(rf_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rf_status hip_fail(hipError_t e, const char* what) {
+  return fail(RF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxTokens = int64_t(1) << 24;  // device index math is exact below this
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+rf_status check_geom(const rf_geom* g) {
+  if (!g) return fail(RF_ERR_NULL, "geometry is NULL");
+  if (g->grid_h < 1 || g->grid_w < 1) return fail(RF_ERR_SHAPE, "grid must be at least 1x1");
+  const int64_t n = (int64_t)g->grid_h * g->grid_w;
+  if (n % 8 != 0) return fail(RF_ERR_SHAPE, "tokens per frame (%lld) must be a multiple of 8", (long long)n);
+  if (n > (int64_t(1) << 20)) return fail(RF_ERR_SHAPE, "tokens per frame too large");
+  if (g->n_heads < 1 || g->n_heads > 1024) return fail(RF_ERR_SHAPE, "n_heads must be in 1..1024");
+  if (g->head_dim != kHeadDim) return fail(RF_ERR_SHAPE, "head_dim must be %d", kHeadDim);
+  for (int a = 0; a < 3; ++a)
+    if (g->rope_pairs[a] < 0) return fail(RF_ERR_SHAPE, "rope_pairs must be >= 0");
+  if (g->rope_pairs[0] + g->rope_pairs[1] + g->rope_pairs[2] != g->head_dim / 2)
+    return fail(RF_ERR_SHAPE, "rope_pairs must sum to head_dim/2");
+  if (!(g->rope_base > 0.0) || !std::isfinite(g->rope_base)) return fail(RF_ERR_SHAPE, "rope_base must be > 0");
+  if (g->max_frame < 1 || g->max_frame > (int64_t(1) << 20))
+    return fail(RF_ERR_SHAPE, "max_frame must be in 1..2^20");
+  return RF_OK;
+}
+
+// cos/sin of pos * base^(-j/P) for pos in [0, npos), j in [0, P): float64 libm, rounded to float32.
+void fill_axis(std::vector<float2>& out, int64_t npos, int P, double base) {
+  std::vector<double> omega(P);
+  for (int j = 0; j < P; ++j) omega[j] = std::pow(base, -((double)j / (double)P));
+  for (int64_t p = 0; p < npos; ++p)
+    for (int j = 0; j < P; ++j) {
+      const double th = (double)p * omega[j];
+      out.push_back(make_float2((float)std::cos(th), (float)std::sin(th)));
+    }
+}
+
+rf_status check_ctx(const rf_ctx* ctx) {
+  if (!ctx) return fail(RF_ERR_NULL, "context is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != ctx->device)
+    return fail(RF_ERR_UNSUPPORTED, "context belongs to device %d, current device is %d", ctx->device, dev);
+  return RF_OK;
+}
+
+rf_status check_tensor(const void* p, int64_t ld, int64_t min_ld, const char* name) {
+  if (!p) return fail(RF_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(RF_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (ld % 8 != 0) return fail(RF_ERR_ALIGN, "%s row stride %lld is not a multiple of 8", name, (long long)ld);
+  if (ld < min_ld) return fail(RF_ERR_SHAPE, "%s row stride %lld < heads*head_dim", name, (long long)ld);
+  return RF_OK;
+}
+
+rf_status check_ring(const rf_kvcache* c, bool need_memory) {
+  if (!c) return fail(RF_ERR_NULL, "cache descriptor is NULL");
+  if (c->capacity < 1) return fail(RF_ERR_SHAPE, "cache capacity must be >= 1");
+  if (c->count < 0 || c->count > c->capacity) return fail(RF_ERR_SHAPE, "cache count outside 0..capacity");
+  if (need_memory) {
+    if (!c->k || !c->v) return fail(RF_ERR_NULL, "cache k/v buffer is NULL");
+    if (!aligned16(c->k) || !aligned16(c->v)) return fail(RF_ERR_ALIGN, "cache buffers must be 16-byte aligned");
+  }
+  return RF_OK;
+}
+
+int64_t mod(int64_t a, int64_t m) {
+  int64_t r = a % m;
+  return r < 0 ? r + m : r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rf_status_string(rf_status s) {
+  switch (s) {
+    case RF_OK: return "RF_OK";
+    case RF_ERR_NULL: return "RF_ERR_NULL";
+    case RF_ERR_ALIGN: return "RF_ERR_ALIGN";
+    case RF_ERR_SHAPE: return "RF_ERR_SHAPE";
+    case RF_ERR_RANGE: return "RF_ERR_RANGE";
+    case RF_ERR_UNSUPPORTED: return "RF_ERR_UNSUPPORTED";
+    case RF_ERR_HIP: return "RF_ERR_HIP";
+  }
+  return "RF_ERR_UNKNOWN";
+}
+
+const char* rf_last_error(void) { return g_err; }
+
+rf_status rf_create(const rf_geom* g, rf_ctx** out) {
+  g_err[0] = 0;
+  if (!out) return fail(RF_ERR_NULL, "out is NULL");
+  rf_status st = check_geom(g);
+  if (st != RF_OK) return st;
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(RF_ERR_UNSUPPORTED, "device %d is %s, librfattn is built for gfx950", dev, prop.gcnArchName);
+
+  std::vector<float2> host;
+  fill_axis(host, g->max_frame, g->rope_pairs[0], g->rope_base);
+  const size_t off_h = host.size();
+  fill_axis(host, g->grid_h, g->rope_pairs[1], g->rope_base);
+  const size_t off_w = host.size();
+  fill_axis(host, g->grid_w, g->rope_pairs[2], g->rope_base);
+  if (host.empty()) host.push_back(make_float2(1.f, 0.f));
+
+  float2* d = nullptr;
+  e = hipMalloc((void**)&d, host.size() * sizeof(float2));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(tables)");
+  e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = prepare_window_attn();
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "table upload / kernel setup");
+  }
+  rf_ctx* c = new rf_ctx;
+  c->g = *g;
+  c->device = dev;
+  c->d_tab = d;
+  c->tab.t = d;
+  c->tab.h = d + off_h;
+  c->tab.w = d + off_w;
+  c->tab.pt = g->rope_pairs[0];
+  c->tab.ph = g->rope_pairs[1];
+  c->tab.pw = g->rope_pairs[2];
+  *out = c;
+  return RF_OK;
+}
+
+void rf_destroy(rf_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipFree(ctx->d_tab);
+  delete ctx;
+}
+
+rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* y, int64_t y_ld,
+                          int64_t t0, int64_t n_tokens, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  const rf_geom& g = ctx->g;
+  const int64_t row = (int64_t)g.n_heads * g.head_dim;
+  if ((st = check_tensor(x, x_ld, row, "x")) != RF_OK) return st;
+  if ((st = check_tensor(y, y_ld, row, "y")) != RF_OK) return st;
+  if (x == y && x_ld != y_ld) return fail(RF_ERR_SHAPE, "in-place RoPE needs y_ld == x_ld");
+  if (n_tokens < 0 || n_tokens >= kMaxTokens) return fail(RF_ERR_SHAPE, "n_tokens must be in 0..2^24-1");
+  if (n_tokens == 0) return RF_OK;
+  const int64_t N = (int64_t)g.grid_h * g.grid_w;
+  if (t0 < 0 || t0 + (n_tokens - 1) / N >= g.max_frame)
+    return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
+                (long long)(t0 + (n_tokens - 1) / N), (long long)g.max_frame);
+  RopeArgs a;
+  a.x = (const uint16_t*)x;
+  a.y = (uint16_t*)y;
+  a.x_ld = x_ld;
+  a.y_ld = y_ld;
+  a.t0 = t0;
+  a.n_tokens = n_tokens;
+  a.N = (int)N;
+  a.gw = g.grid_w;
+  a.H = g.n_heads;
+  a.tab = ctx->tab;
+  hipError_t e = launch_rope3d(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  return RF_OK;
+}
+
+rf_status rf_kvcache_plan_roll(const rf_kvcache* c, int64_t t0, int32_t n_frames, rf_kvcache* after) {
+  g_err[0] = 0;
+  rf_status st = check_ring(c, false);
+  if (st != RF_OK) return st;
+  if (!after) return fail(RF_ERR_NULL, "after is NULL");
+  if (n_frames < 1 || n_frames > c->capacity)
+    return fail(RF_ERR_SHAPE, "n_frames must be in 1..capacity (%d)", c->capacity);
+  int64_t first = c->first;
+  int64_t end = c->first + c->count;  // one past the newest valid frame
+  if (c->count == 0) {
+    first = t0;
+    end = t0;
+  } else if (t0 < c->first || t0 > end) {
+    return fail(RF_ERR_RANGE, "roll start %lld outside %lld..%lld", (long long)t0, (long long)c->first,
+                (long long)end);
+  }
+  const int64_t new_end = std::max(end, t0 + n_frames);
+  int64_t count = new_end - first;
+  if (count > c->capacity) {  // appends to a full ring evict the oldest frames
+    first = new_end - c->capacity;
+    count = c->capacity;
+  }
+  *after = *c;
+  after->first = first;
+  after->count = (int32_t)count;
+  return RF_OK;
+}
+
+rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, int64_t k_ld,
+                          const void* v_new, int64_t v_ld, int64_t t0, int32_t n_frames, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if ((st = check_ring(c, true)) != RF_OK) return st;
+  const rf_geom& g = ctx->g;
+  const int64_t row = (int64_t)g.n_heads * g.head_dim;
+  if ((st = check_tensor(k_new, k_ld, row, "k_new")) != RF_OK) return st;
+  if ((st = check_tensor(v_new, v_ld, row, "v_new")) != RF_OK) return st;
+  rf_kvcache after;
+  if ((st = rf_kvcache_plan_roll(c, t0, n_frames, &after)) != RF_OK) return st;
+  if (t0 < 0 || t0 + n_frames > g.max_frame)
+    return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
+                (long long)(t0 + n_frames - 1), (long long)g.max_frame);
+  const int64_t N = (int64_t)g.grid_h * g.grid_w;
+  if ((int64_t)n_frames * N >= kMaxTokens) return fail(RF_ERR_SHAPE, "too many tokens in one roll");
+  if ((int64_t)n_frames * g.n_heads > 65535) return fail(RF_ERR_SHAPE, "n_frames*n_heads must be <= 65535");
+
+  RollArgs a;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_ld = k_ld;
+  a.v_ld = v_ld;
+  a.k_ring = (uint16_t*)c->k;
+  a.v_ring = (uint16_t*)c->v;
+  a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;
+  a.t0 = t0;
+  a.slot0 = (int)mod(t0, c->capacity);
+  a.n_frames = n_frames;
+  a.W = c->capacity;
+  a.N = (int)N;
+  a.gw = g.grid_w;
+  a.H = g.n_heads;
+  a.tab = ctx->tab;
+  hipError_t e = launch_roll(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kvcache roll launch");
+  c->first = after.first;
+  c->count = after.count;
+  return RF_OK;
+}
+
+rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs,
+                              int32_t n_segs, float scale, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if ((st = check_ring(c, true)) != RF_OK) return st;
+  if (!segs) return fail(RF_ERR_NULL, "segments is NULL");
+  if (n_segs < 1 || n_segs > RF_MAX_SEGMENTS)
+    return fail(RF_ERR_SHAPE, "n_segs must be in 1..%d", RF_MAX_SEGMENTS);
+  if (scale == 0.0f) scale = 1.0f / std::sqrt((float)ctx->g.head_dim);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(RF_ERR_SHAPE, "scale must be > 0 and finite");
+  if (c->count == 0) return fail(RF_ERR_RANGE, "the cache holds no frames");
+
+  const rf_geom& g = ctx->g;
+  const int64_t N = (int64_t)g.grid_h * g.grid_w;
+  const int64_t row = (int64_t)g.n_heads * g.head_dim;
+  const int bm = window_attn_block_m();
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int64_t tiles = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const rf_attn_segment& s = segs[i];
+    if ((st = check_tensor(s.q, s.q_ld, row, "q")) != RF_OK) return st;
+    if ((st = check_tensor(s.o, s.o_ld, row, "o")) != RF_OK) return st;
+    if (s.q_frames < 1 || s.ctx_frames < 1) return fail(RF_ERR_SHAPE, "segment %d: frames must be >= 1", i);
+    if ((int64_t)s.q_frames * N >= kMaxTokens) return fail(RF_ERR_SHAPE, "segment %d: too many query tokens", i);
+    if (s.q_t0 < 0 || s.q_t0 + s.q_frames > g.max_frame)
+      return fail(RF_ERR_RANGE, "segment %d: query frames outside the tables", i);
+    if (s.ctx_t0 < c->first || s.ctx_t0 + s.ctx_frames > c->first + c->count)
+      return fail(RF_ERR_RANGE, "segment %d: context %lld..%lld outside the window %lld..%lld", i,
+                  (long long)s.ctx_t0, (long long)(s.ctx_t0 + s.ctx_frames - 1), (long long)c->first,
+                  (long long)(c->first + c->count - 1));
+    SegDev& d = a.seg[i];
+    d.q = (const uint16_t*)s.q;
+    d.o = (uint16_t*)s.o;
+    d.q_ld = s.q_ld;
+    d.o_ld = s.o_ld;
+    d.q_t0 = s.q_t0;
+    d.q_tokens = (int)(s.q_frames * N);
+    d.q_tiles = (int)((d.q_tokens + bm - 1) / bm);
+    d.tile_begin = (int)tiles;
+    d.ctx_keys = (int)(s.ctx_frames * N);
+    d.ctx_slot0 = (int)mod(s.ctx_t0, c->capacity);
+    tiles += (int64_t)d.q_tiles * g.n_heads;
+    if (tiles > (int64_t(1) << 30)) return fail(RF_ERR_SHAPE, "grid too large");
+  }
+  a.n_segs = n_segs;
+  a.total_tiles = (int)tiles;
+  a.k_ring = (const uint16_t*)c->k;
+  a.v_ring = (const uint16_t*)c->v;
+  a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;
+  a.W = c->capacity;
+  a.N = (int)N;
+  a.gw = g.grid_w;
+  a.H = g.n_heads;
+  a.c_log2 = scale * 1.4426950408889634f;
+  a.tab = ctx->tab;
+  hipError_t e = launch_window_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  return RF_OK;
+}
+
+}  // extern "C"

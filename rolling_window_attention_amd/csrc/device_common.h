@@ -1,0 +1,91 @@
+// Device helpers shared by the librfattn kernels (gfx950 only).
+//
+// * bf16 <-> float conversions on raw 16-bit patterns;
+// * the bit-exact 3D-RoPE rotation of one 16-byte chunk (4 rotation pairs);
+// * small exact integer division for token -> (frame, row, column).
+//
+// 3D-RoPE over (time, height, width): "Amazon and Reactor tune Trainium for
+// real-time video generation", section "Three problems for generic compilers".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rfattn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// cos/sin tables, float2 = (cos, sin) of pos * base^(-j/P), rounded to float32.
+struct RopeTables {
+  const float2* t;  // [max_frame][pt]
+  const float2* h;  // [grid_h][ph]
+  const float2* w;  // [grid_w][pw]
+  int pt, ph, pw;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float64 -> bf16, round to nearest even, taken directly (no double rounding).
+// The float32 conversion rounds to nearest even; that can only mislead the
+// second rounding when it lands exactly on a bf16 halfway point (low 16 bits
+// 0x8000) without being exact.  In that case the float32 pattern is nudged
+// one float32 ulp towards the true value before the float32 -> bf16 rounding.
+// Finite inputs only (NaN/Inf are not produced by the library's arithmetic
+// on finite bf16 inputs of moderate size).
+__device__ __forceinline__ uint32_t f64_to_bf16(double y) {
+  float f = (float)y;
+  uint32_t fb = __float_as_uint(f);
+  if ((fb & 0xFFFFu) == 0x8000u) {
+    double back = (double)f;
+    if (back != y) fb += (fabs(y) > fabs(back)) ? 1u : 0xFFFFFFFFu;
+  }
+  return (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
+}
+
+// (cos, sin) of rotation pair p for a token at (frame t, row r, column c).
+__device__ __forceinline__ float2 rope_cs(const RopeTables& T, int p, int64_t t, int r, int c) {
+  const float2* ptr;
+  if (p < T.pt) {
+    ptr = T.t + t * T.pt + p;
+  } else if (p < T.pt + T.ph) {
+    ptr = T.h + (int64_t)r * T.ph + (p - T.pt);
+  } else {
+    ptr = T.w + (int64_t)c * T.pw + (p - T.pt - T.ph);
+  }
+  return *ptr;
+}
+
+// Rotate one 16-byte chunk (8 bf16 = pairs p0..p0+3) of a token at (t, r, c):
+//   y0 = bf16(fl64(x0*c - x1*s)),  y1 = bf16(fl64(x0*s + x1*c)).
+// bf16*float32 products carry at most 32 significant bits, so they are exact
+// in float64; whether the compiler contracts to FMA does not change results.
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, int p0, int64_t t, int r, int c,
+                                            const RopeTables& T) {
+  uint32_t in[4] = {x[0], x[1], x[2], x[3]};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float2 cs = rope_cs(T, p0 + k, t, r, c);
+    double x0 = (double)bf16_to_f32(in[k] & 0xFFFFu);
+    double x1 = (double)bf16_to_f32(in[k] >> 16);
+    double cc = (double)cs.x, ss = (double)cs.y;
+    double y0 = x0 * cc - x1 * ss;
+    double y1 = x0 * ss + x1 * cc;
+    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+  }
+  u32x4 y = {out[0], out[1], out[2], out[3]};
+  return y;
+}
+
+// Exact unsigned division n / d for n < 2^24, d >= 1: a float estimate is off
+// by at most one and is corrected with one multiply-subtract.
+__device__ __forceinline__ uint32_t small_div(uint32_t n, uint32_t d, float inv_d, uint32_t* rem) {
+  uint32_t q = (uint32_t)((float)n * inv_d);
+  int32_t r = (int32_t)(n - q * d);
+  if (r < 0) { q -= 1; r += (int32_t)d; }
+  if (r >= (int32_t)d) { q += 1; r -= (int32_t)d; }
+  *rem = (uint32_t)r;
+  return q;
+}
+
+}  // namespace rfattn

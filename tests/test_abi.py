@@ -1,0 +1,112 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point the
+header declares, and its host-side validation and ring bookkeeping behave (no GPU call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rolling_window_attention_amd as rf
+from oracle.ring import RingError, RingModel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rfattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rf.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return rf.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(rf_[a-z0-9_]+)\s*\(", src))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(rf.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    # and they are real exported functions of the shared object
+    out = os.popen(f"nm -D --defined-only {rf.LIB_PATH}").read()
+    for name in _declared():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings(L):
+    for code, name in rf.STATUS_NAMES.items():
+        assert L.rf_status_string(code).decode() == name
+    assert L.rf_status_string(99).decode() == "RF_ERR_UNKNOWN"
+
+
+def _geom(**kw):
+    d = dict(grid_h=30, grid_w=52, n_heads=12, head_dim=128, pairs=(22, 21, 21), base=1e4,
+             max_frame=4096)
+    d.update(kw)
+    return rf.Geom(d["grid_h"], d["grid_w"], d["n_heads"], d["head_dim"],
+                   (ctypes.c_int32 * 3)(*d["pairs"]), d["base"], d["max_frame"])
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=64, pairs=(11, 11, 10)), dict(pairs=(22, 21, 20)),
+                                dict(pairs=(-1, 43, 22)), dict(grid_h=5, grid_w=5),
+                                dict(grid_h=0), dict(n_heads=0), dict(base=0.0),
+                                dict(base=float("nan")), dict(max_frame=0),
+                                dict(max_frame=1 << 21)])
+def test_create_rejects_bad_geometry_before_touching_a_device(L, kw):
+    g = _geom(**kw)
+    h = ctypes.c_void_p()
+    st = L.rf_create(ctypes.byref(g), ctypes.byref(h))
+    assert st == 3, rf.STATUS_NAMES.get(st)
+    assert h.value is None
+    assert L.rf_last_error().decode()
+
+
+def test_null_arguments(L):
+    h = ctypes.c_void_p()
+    assert L.rf_create(None, ctypes.byref(h)) == 1
+    assert L.rf_create(ctypes.byref(_geom()), None) == 1
+    assert L.rf_rope3d_apply(None, None, 1536, None, 1536, 0, 1, None) == 1
+    assert L.rf_window_attention(None, None, None, 1, 0.0, None) == 1
+    assert L.rf_kvcache_roll(None, None, None, 1536, None, 1536, 0, 1, None) == 1
+    L.rf_destroy(None)  # ignored
+
+
+def test_plan_roll_matches_oracle_ring_model(L):
+    rng = np.random.default_rng(0)
+    for W in (1, 3, 5, 21):
+        for _ in range(300):
+            model = RingModel(W)
+            first, count = 0, 0
+            for _ in range(int(rng.integers(1, 10))):
+                if model.count == 0:
+                    t0 = int(rng.integers(0, 100))
+                else:
+                    t0 = int(rng.integers(model.first - 2, model.first + model.count + 3))
+                n = int(rng.integers(0, W + 2))
+                try:
+                    model.check_roll(t0, n)
+                    ok = True
+                except RingError:
+                    ok = False
+                if ok:
+                    model.roll(t0, n)
+                    first, count = rf.plan_roll(W, first, count, t0, n)
+                    assert (first, count) == (model.first, model.count)
+                else:
+                    with pytest.raises(rf.RfError):
+                        rf.plan_roll(W, first, count, t0, n)
+
+
+def test_plan_roll_rejects_bad_descriptors(L):
+    with pytest.raises(rf.RfError):
+        rf.plan_roll(0, 0, 0, 0, 1)
+    with pytest.raises(rf.RfError):
+        rf.plan_roll(5, 0, 6, 0, 1)

@@ -1,0 +1,310 @@
+"""GPU parity of rf_window_attention against the float64 oracle.
+
+Tolerances (max-abs 2e-2, mean-abs 2e-3 on bf16 inputs) plus rel-L2 <= 1e-2, because at
+32,760 keys the output's own spread is ~0.01 and dropping a whole context frame would still
+pass the absolute bounds.  Closed-form checks on top: q = 0 returns the mean of the attended
+values (frame tags prove which frames were read) and k = 16q makes every query pick its own
+token's value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rolling_window_attention_amd as rf
+from rolling_window_attention_amd import synth
+from oracle import attention as oatt
+
+from gpu_util import (RotatedKeys, assert_close, down, f64, oracle_rows, sample_rows, up)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ctx(g, max_frame=4096):
+    return rf.Context(g.grid_h, g.grid_w, g.n_heads, g.head_dim, g.pairs, g.base, max_frame)
+
+
+def _out(g, n_frames):
+    return torch.empty((n_frames * g.tokens_per_frame, g.n_heads, g.head_dim), dtype=torch.bfloat16,
+                       device="cuda")
+
+
+def test_tiny_full_parity():
+    """6x8 grid, 2 cached + 3 current frames (240 keys), 3 query frames (144 rows)."""
+    g, cfg = synth.TINY, synth.WORKLOAD_IDS["tiny"]
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    kc = synth.frames(g, cfg, 0, 0, 2, synth.K + synth.CLEAN)
+    vc = synth.frames(g, cfg, 0, 0, 2, synth.V + synth.CLEAN)
+    cache.roll(up(kc), up(vc), 0)
+    k = synth.frames(g, cfg, 1, 2, 3, synth.K)
+    v = synth.frames(g, cfg, 1, 2, 3, synth.V)
+    q = synth.frames(g, cfg, 1, 2, 3, synth.Q)
+    cache.roll(up(k), up(v), 2)
+    o = _out(g, 3)
+    rf.window_attention(ctx, cache, [rf.Segment(up(q), 2, o, 0, 5)])
+    torch.cuda.synchronize()
+    want = oatt.window_attention(f64(q), 2, f64(np.concatenate([kc, k])),
+                                 f64(np.concatenate([vc, v])), 0, g.grid_h, g.grid_w, g.pairs,
+                                 g.base)
+    assert_close(f64(down(o)), want, "tiny")
+
+
+def test_tiny_wrap_run_and_two_segments():
+    """Twelve steps on a 5-slot ring: each step rolls the clean frame s-1 and the current
+    frames s..s+2, then ONE launch runs the denoise segment (3 frames) and the cache-update
+    segment (frame s-1) over the window; every output row is checked."""
+    g, cfg = synth.TINY, 11
+    W, N = g.window, g.tokens_per_frame
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, W)
+    frames_k, frames_v = {}, {}
+    for s in range(12):
+        t0 = max(s - 1, 0)
+        ts = list(range(t0, s + 3))
+        for t in ts:
+            tag = synth.CLEAN if t < s else 0
+            frames_k[t] = synth.frame(g, cfg, s, t, synth.K + tag)
+            frames_v[t] = synth.frame(g, cfg, s, t, synth.V + tag)
+        cache.roll(up(np.concatenate([frames_k[t] for t in ts])),
+                   up(np.concatenate([frames_v[t] for t in ts])), t0)
+        lo, hi = cache.first, cache.first + cache.count  # window [lo, hi)
+        qa = synth.frames(g, cfg, s, s, 3, synth.Q)
+        oa = _out(g, 3)
+        segs = [rf.Segment(up(qa), s, oa, lo, hi - lo)]
+        if s >= 1:
+            qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
+            ob = _out(g, 1)
+            segs.append(rf.Segment(up(qb), s - 1, ob, lo, hi - lo))
+        print(f"step {s}: window [{lo},{hi}) segments={len(segs)}", flush=True)
+        rf.window_attention(ctx, cache, segs)
+        torch.cuda.synchronize()
+        kk = f64(np.concatenate([frames_k[t] for t in range(lo, hi)]))
+        vv = f64(np.concatenate([frames_v[t] for t in range(lo, hi)]))
+        want = oatt.window_attention(f64(qa), s, kk, vv, lo, g.grid_h, g.grid_w, g.pairs, g.base)
+        assert_close(f64(down(oa)), want, f"step {s} A")
+        if s >= 1:
+            want = oatt.window_attention(f64(qb), s - 1, kk, vv, lo, g.grid_h, g.grid_w, g.pairs,
+                                         g.base)
+            assert_close(f64(down(ob)), want, f"step {s} B")
+
+
+@pytest.mark.parametrize("geom", [synth.TINY, synth.FULL])
+def test_zero_query_reads_exactly_the_context_frames(geom):
+    """q = 0: every weight is 1, so o = mean of v over the context.  v of frame t is the
+    constant t/32 (exact in bf16), so the output names the attended frames."""
+    g = geom
+    W, N, H, D = g.window, g.tokens_per_frame, g.n_heads, g.head_dim
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, W)
+    t_end = W + 3  # roll frames 0..W+2 one by one, so the ring has wrapped
+    for t in range(t_end):
+        k = synth.frame(g, 5, 0, t, synth.K)
+        v = np.full((N, H, D), t / 32.0)
+        cache.roll(up(k), up(synth.f32_to_bf16_bits(v.astype(np.float32))), t)
+    lo, hi = t_end - W, t_end
+    assert cache.window() == list(range(lo, hi))
+    q = torch.zeros((N, H, D), dtype=torch.bfloat16, device="cuda")
+    for ctx_t0, nf in ((lo, W), (hi - 3, 3), (lo + 1, 1), (lo + 1, W - 2)):
+        o = _out(g, 1)
+        rf.window_attention(ctx, cache, [rf.Segment(q, 4, o, ctx_t0, nf)])
+        torch.cuda.synchronize()
+        want = np.mean(np.arange(ctx_t0, ctx_t0 + nf)) / 32.0
+        got = f64(down(o))
+        print(f"ctx {ctx_t0}+{nf}: want {want:.6f} got [{got.min():.6f}, {got.max():.6f}]", flush=True)
+        assert np.all(np.abs(got - want) <= abs(want) * 2.0 ** -7), (ctx_t0, nf)
+
+
+@pytest.mark.parametrize("geom,nf", [(synth.TINY, 4), (synth.FULL, 4)])
+def test_self_match(geom, nf):
+    """Context = the query frames and k = 16 q token by token, with every q row scaled to
+    norm sqrt(D).  RoPE cancels at equal positions, so a query's own key scores
+    16*sqrt(D) ~ 181 while the others score ~N(0, 16^2): each query must return its own
+    token's v row."""
+    g = geom
+    W, N, H, D = g.window, g.tokens_per_frame, g.n_heads, g.head_dim
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, W)
+    t0 = 30
+    x = np.random.default_rng(77).standard_normal((nf * N, H, D))
+    x *= np.sqrt(D) / np.linalg.norm(x, axis=2, keepdims=True)
+    q = synth.f32_to_bf16_bits(x.astype(np.float32))
+    k = synth.f32_to_bf16_bits((f64(q) * 16.0).astype(np.float32))  # exact: power of two
+    v = synth.frames(g, 6, 0, t0, nf, synth.V)
+    cache.roll(up(k), up(v), t0)
+    o = _out(g, nf)
+    rf.window_attention(ctx, cache, [rf.Segment(up(q), t0, o, t0, nf)])
+    torch.cuda.synchronize()
+    got = f64(down(o))
+    want = f64(v)
+    err = np.abs(got - want).max()
+    print(f"self-match max_abs={err:.3e}", flush=True)
+    assert err <= 2.0 ** -7 * np.abs(want).max()
+
+
+def _fill_steady(g, cfg, s, cache):
+    """Bring `cache` to the state after step s: clean frames max(0,s-6)..s-1 (as written at
+    steps t+1), current frames s..s+14 drawn at step s.  Returns {t: (k_bits, v_bits, tag)}."""
+    N = g.tokens_per_frame
+    lo = max(0, s - 6)
+    data = {}
+    for t in range(lo, s):
+        data[t] = (synth.frame(g, cfg, t + 1, t, synth.K + synth.CLEAN),
+                   synth.frame(g, cfg, t + 1, t, synth.V + synth.CLEAN), ("clean", t + 1))
+    for t in range(s, s + 15):
+        data[t] = (synth.frame(g, cfg, s, t, synth.K), synth.frame(g, cfg, s, t, synth.V),
+                   ("noisy", s))
+    ts = sorted(data)
+    # two rolls: clean frames, then the current ones (each <= 21 frames)
+    if lo < s:
+        cache.roll(up(np.concatenate([data[t][0] for t in range(lo, s)])),
+                   up(np.concatenate([data[t][1] for t in range(lo, s)])), lo)
+    cache.roll(up(np.concatenate([data[t][0] for t in range(s, s + 15)])),
+               up(np.concatenate([data[t][1] for t in range(s, s + 15)])), s)
+    assert cache.window() == ts
+    return data
+
+
+def _check_rows(g, rk, data, q_bits, q_t0, o, ctx_lo, ctx_hi, rows, what):
+    khs = [rk.get(t, data[t][2], data[t][0]) for t in range(ctx_lo, ctx_hi)]
+    vs = [data[t][1] for t in range(ctx_lo, ctx_hi)]
+    want = oracle_rows(g, q_bits, q_t0, khs, vs, rows)
+    got = f64(down(o))[rows]
+    assert_close(got, want, what)
+
+
+def test_cache_update_pass_full_size():
+    """1 clean query frame (1,560 rows) over 21 frames (32,760 keys), after a roll that
+    evicts the oldest frame; sampled rows incl. frame and tile edges."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["cache_update"]
+    W, N = g.window, g.tokens_per_frame
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, W)
+    data = {}
+    for t in range(W):
+        data[t] = (synth.frame(g, cfg, 0, t, synth.K), synth.frame(g, cfg, 0, t, synth.V), 0)
+    cache.roll(up(np.concatenate([data[t][0] for t in range(W)])),
+               up(np.concatenate([data[t][1] for t in range(W)])), 0)
+    data[21] = (synth.frame(g, cfg, 1, 21, synth.K + synth.CLEAN),
+                synth.frame(g, cfg, 1, 21, synth.V + synth.CLEAN), 1)
+    cache.roll(up(data[21][0]), up(data[21][1]), 21)
+    assert cache.window() == list(range(1, 22))
+    q = synth.frame(g, cfg, 1, 21, synth.Q + synth.CLEAN)
+    o = _out(g, 1)
+    rf.window_attention(ctx, cache, [rf.Segment(up(q), 21, o, 1, 21)])
+    torch.cuda.synchronize()
+    rows = sample_rows(N, N, extra=96, seed=1)
+    _check_rows(g, RotatedKeys(g), data, q, 21, o, 1, 22, rows, "cache-update")
+
+
+def test_denoise_pass_full_size_and_determinism():
+    """15 query frames (23,400 rows) over 21 frames (32,760 keys) = 6 cached + 15 current."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["denoise"]
+    N = g.tokens_per_frame
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    data = _fill_steady(g, cfg, 6, cache)
+    q = synth.frames(g, cfg, 6, 6, 15, synth.Q)
+    qd = up(q)
+    o = _out(g, 15)
+    rf.window_attention(ctx, cache, [rf.Segment(qd, 6, o, 0, 21)])
+    o2 = _out(g, 15)
+    rf.window_attention(ctx, cache, [rf.Segment(qd, 6, o2, 0, 21)])
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "not deterministic"
+    rows = sample_rows(15 * N, N, extra=160, seed=2)
+    _check_rows(g, RotatedKeys(g), data, q, 6, o, 0, 21, rows, "denoise")
+
+
+def test_batched_two_phase_step_full_size():
+    """Steady state step s = 9: ONE launch with the denoise segment (frames 9..23) and the
+    cache-update segment (frame 8), both over the window 3..23."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["batched"]
+    N = g.tokens_per_frame
+    s = 9
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    # bring the ring to the state before step s, then roll frame s-1 (clean) + s..s+14
+    _fill_steady(g, cfg, s - 1, cache)
+    data = {}
+    for t in range(s - 6, s):
+        data[t] = (synth.frame(g, cfg, t + 1, t, synth.K + synth.CLEAN),
+                   synth.frame(g, cfg, t + 1, t, synth.V + synth.CLEAN), ("clean", t + 1))
+    for t in range(s, s + 15):
+        data[t] = (synth.frame(g, cfg, s, t, synth.K), synth.frame(g, cfg, s, t, synth.V),
+                   ("noisy", s))
+    cache.roll(up(np.concatenate([data[t][0] for t in range(s - 1, s + 15)])),
+               up(np.concatenate([data[t][1] for t in range(s - 1, s + 15)])), s - 1)
+    assert cache.window() == list(range(s - 6, s + 15))
+    qa = synth.frames(g, cfg, s, s, 15, synth.Q)
+    qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
+    oa, ob = _out(g, 15), _out(g, 1)
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), s, oa, s - 6, 21),
+                                     rf.Segment(up(qb), s - 1, ob, s - 6, 21)])
+    torch.cuda.synchronize()
+    rk = RotatedKeys(g)
+    _check_rows(g, rk, data, qa, s, oa, s - 6, s + 15, sample_rows(15 * N, N, extra=96, seed=3),
+                "batched A")
+    _check_rows(g, rk, data, qb, s - 1, ob, s - 6, s + 15, sample_rows(N, N, extra=64, seed=4),
+                "batched B")
+
+
+def test_dynamic_window_fill_30_steps():
+    """30 steps in one process: context grows 15..21 frames as the ring fills, then one
+    frame is evicted per step; no reallocation between steps.  Sampled rows every step."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["dynamic"]
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    kbuf = torch.empty((16 * N, H, D), dtype=torch.bfloat16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    qbuf = torch.empty((15 * N, H, D), dtype=torch.bfloat16, device="cuda")
+    o = _out(g, 15)
+    rk = RotatedKeys(g)
+    data = {}
+    mem0 = None
+    for s in range(30):
+        t0 = max(s - 1, 0)
+        for t in range(t0, s + 15):
+            tag = ("clean", s) if t < s else ("noisy", s)
+            tid = synth.CLEAN if t < s else 0
+            data[t] = (synth.frame(g, cfg, s, t, synth.K + tid), synth.frame(g, cfg, s, t, synth.V + tid), tag)
+        n = s + 15 - t0
+        kbuf[:n * N] = up(np.concatenate([data[t][0] for t in range(t0, s + 15)]))
+        vbuf[:n * N] = up(np.concatenate([data[t][1] for t in range(t0, s + 15)]))
+        cache.roll(kbuf[:n * N], vbuf[:n * N], t0)
+        lo = s - min(s, 6)
+        assert cache.window() == list(range(lo, s + 15)), (s, cache.window())
+        q = synth.frames(g, cfg, s, s, 15, synth.Q)
+        qbuf.copy_(up(q))
+        rf.window_attention(ctx, cache, [rf.Segment(qbuf, s, o, lo, s + 15 - lo)])
+        torch.cuda.synchronize()
+        if mem0 is None:
+            mem0 = torch.cuda.memory_allocated()
+        assert torch.cuda.memory_allocated() == mem0
+        rows = sample_rows(15 * N, N, extra=8, seed=100 + s) if s in (0, 6, 7, 29) else \
+            np.array([0, 777, 15 * N - 1])
+        rk.prune(lo)
+        print(f"step {s}: ctx {s + 15 - lo} frames, {len(rows)} rows", flush=True)
+        _check_rows(g, rk, data, q, s, o, lo, s + 15, rows, f"dynamic step {s}")
+
+
+def test_attention_errors():
+    g = synth.TINY
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    q = up(synth.frames(g, 9, 0, 0, 1, synth.Q))
+    o = _out(g, 1)
+    with pytest.raises(rf.RfError) as e:  # empty cache
+        rf.window_attention(ctx, cache, [rf.Segment(q, 0, o, 0, 1)])
+    assert e.value.status == 4
+    k = up(synth.frames(g, 9, 0, 0, 3, synth.K))
+    cache.roll(k, k, 0)
+    for ctx_t0, nf in ((0, 4), (-1, 2), (3, 1)):
+        with pytest.raises(rf.RfError) as e:
+            rf.window_attention(ctx, cache, [rf.Segment(q, 0, o, ctx_t0, nf)])
+        assert e.value.status == 4
+    with pytest.raises(rf.RfError) as e:
+        rf.window_attention(ctx, cache, [rf.Segment(q, 0, o, 0, 3)], scale=-1.0)
+    assert e.value.status == 3
+    with pytest.raises(ValueError):
+        rf.window_attention(ctx, cache, [])
