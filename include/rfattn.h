@@ -107,7 +107,7 @@ const char* rf_last_error(void);
  *   y[2p+1] = bf16_rne( fl64( x[2p]*s + x[2p+1]*c ) )
  * with c, s the float32 table entries; the products are exact in float64,
  * so the result is unique and reproducible bit for bit.
- * n_tokens == 0 is a no-op.  Errors: RF_ERR_NULL, RF_ERR_ALIGN,
+ * n_tokens == 0 is a no-op (x and y are not examined).  Errors: RF_ERR_NULL, RF_ERR_ALIGN,
  * RF_ERR_SHAPE (ld too small, n_tokens < 0), RF_ERR_RANGE (t0 < 0 or the
  * last token's frame >= max_frame).
  */

@@ -189,11 +189,11 @@ rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* 
   if (st != RF_OK) return st;
   const rf_geom& g = ctx->g;
   const int64_t row = (int64_t)g.n_heads * g.head_dim;
+  if (n_tokens < 0 || n_tokens >= kMaxTokens) return fail(RF_ERR_SHAPE, "n_tokens must be in 0..2^24-1");
+  if (n_tokens == 0) return RF_OK;  // nothing to touch: pointers may be NULL
   if ((st = check_tensor(x, x_ld, row, "x")) != RF_OK) return st;
   if ((st = check_tensor(y, y_ld, row, "y")) != RF_OK) return st;
   if (x == y && x_ld != y_ld) return fail(RF_ERR_SHAPE, "in-place RoPE needs y_ld == x_ld");
-  if (n_tokens < 0 || n_tokens >= kMaxTokens) return fail(RF_ERR_SHAPE, "n_tokens must be in 0..2^24-1");
-  if (n_tokens == 0) return RF_OK;
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
   if (t0 < 0 || t0 + (n_tokens - 1) / N >= g.max_frame)
     return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,

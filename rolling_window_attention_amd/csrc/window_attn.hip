@@ -30,6 +30,8 @@
 namespace rfattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -42,16 +44,53 @@ constexpr int kKTile = kBlockN * kKRow;    // elements
 constexpr int kVTile = kHeadDim * kVRow;   // elements
 constexpr int kStage = kKTile + kVTile;    // one LDS buffer, elements
 constexpr size_t kLdsBytes = 2 * kStage * sizeof(uint16_t);
+constexpr float kRescaleLog2 = 8.0f;       // rescale O only when a row max grows by > 2^8
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // buffer offset past the end: the load returns 0
+constexpr int kXcds = 8;                   // MI355X: work-groups go round-robin over 8 XCDs
 
 int window_attn_block_m() { return kBlockM; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// Combine a per-lane value with the lane 32 positions away (the other half of the
+// wave holds the other 16 keys of the same query).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Work-group id -> tile index such that each XCD walks a contiguous run of tiles
+// (consecutive query tiles of one head), so the work-groups resident on an XCD at
+// any time share their head's K/V in that XCD's L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int per = (total + kXcds - 1) / kXcds;
+  const int rem = total % kXcds;
+  const int x = bid % kXcds, idx = bid / kXcds;
+  if (rem == 0 || x < rem) return x * per + idx;
+  return rem * per + (x - rem) * (per - 1) + idx;
+}
+
+// kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
+// general per-row frame walk is used.  Otherwise a tile straddles at most one
+// frame boundary and each row picks one of two bases.
+template <bool kSmallN>
 __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int tid = threadIdx.x;
@@ -61,13 +100,13 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   const int hf = lane >> 5;  // lane half: selects k-slots 0-7 / 8-15 of an MFMA step
 
   // ---- work-group -> (segment, head, query tile) ---------------------------
-  const int bid = blockIdx.x;
+  const int tile = xcd_tile(blockIdx.x, a.total_tiles);
   int si = 0;
 #pragma unroll
   for (int s = 1; s < kMaxSegments; ++s)
-    if (s < a.n_segs && bid >= a.seg[s].tile_begin) si = s;
+    if (s < a.n_segs && tile >= a.seg[s].tile_begin) si = s;
   const SegDev& sg = a.seg[si];
-  const int local = bid - sg.tile_begin;
+  const int local = tile - sg.tile_begin;
   const int h = local / sg.q_tiles;
   const int qt = local - h * sg.q_tiles;
 
@@ -92,55 +131,72 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
     for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
-  // ---- tile loaders ----------------------------------------------------------
+  // ---- tile loaders (byte offsets into the rings, raw buffer loads) ------------
   const int nkeys = sg.ctx_keys;
   const int ntiles = (nkeys + kBlockN - 1) / kBlockN;
   const int N = a.N;
   const int W = a.W;
-  const uint16_t* kbase = a.k_ring + (int64_t)h * N * kHeadDim;
-  const uint16_t* vbase = a.v_ring + (int64_t)h * kHeadDim * N;
+  const uint32_t slot_b = (uint32_t)a.slot_elems * 2u;
+  const uint32_t ring_b = slot_b * (uint32_t)W;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_ring), 0, (int)ring_b, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_ring), 0, (int)ring_b, kBufferWord3);
+  const uint32_t k_head = (uint32_t)h * (uint32_t)N * (kHeadDim * 2u);  // K: [H][N][D]
+  const uint32_t v_head = (uint32_t)h * kHeadDim * (uint32_t)N * 2u;    // V: [H][D][N]
   // K: rows (tid>>4) + 16i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 32i, key chunk tid&7.
   const int k_r0 = tid >> 4, k_c = tid & 15;
   const int v_d0 = tid >> 3, v_kc = tid & 7;
   u32x4 kst[4], vst[4];
 
-  // Cursor of the tile start in the key stream: slot and token offset.
+  // Cursor of the tile start in the key stream (uniform): slot and token offset.
   int cur_slot = sg.ctx_slot0;
   int cur_n = 0;
 
-  auto locate = [&](int off, int& slot, int& n) {
-    n = cur_n + off;
-    slot = cur_slot;
-    while (n >= N) {
-      n -= N;
-      slot = (slot + 1 == W) ? 0 : slot + 1;
-    }
-  };
-
   auto load_tile = [&](int kt) {
-    const int key0 = kt * kBlockN;
+    const int key_lim = nkeys - kt * kBlockN;  // valid keys in this tile
+    uint32_t koff[4], voff[4];
+    if constexpr (!kSmallN) {
+      const int b = N - cur_n;  // keys of this tile still in the current frame
+      const int nxt = (cur_slot + 1 == W) ? 0 : cur_slot + 1;
+      const uint32_t ka = (uint32_t)cur_slot * slot_b + k_head + (uint32_t)cur_n * (kHeadDim * 2u);
+      const uint32_t kb = (uint32_t)nxt * slot_b + k_head - (uint32_t)b * (kHeadDim * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = k_r0 + 16 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key0 + r < nkeys) {
-        int slot, n;
-        locate(r, slot, n);
-        v = *(const u32x4*)(kbase + slot * a.slot_elems + (int64_t)n * kHeadDim + 8 * k_c);
+      for (int i = 0; i < 4; ++i) {
+        const int r = k_r0 + 16 * i;
+        koff[i] = (uint32_t)r * (kHeadDim * 2u) + 16u * k_c + (r < b ? ka : kb);
       }
-      kst[i] = v;
+      const uint32_t vbase = (8 * v_kc < b)
+                                 ? (uint32_t)cur_slot * slot_b + v_head + (uint32_t)cur_n * 2u
+                                 : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        voff[i] = vbase + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u + 16u * v_kc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int n = cur_n + k_r0 + 16 * i, slot = cur_slot;
+        while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
+        koff[i] = (uint32_t)slot * slot_b + k_head + (uint32_t)n * (kHeadDim * 2u) + 16u * k_c;
+      }
+      int n = cur_n + 8 * v_kc, slot = cur_slot;
+      while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)slot * slot_b + v_head + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u +
+                  (uint32_t)n * 2u;
+    }
+    if (key_lim < kBlockN) {  // last tile: keys past the end read as zeros
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k_r0 + 16 * i >= key_lim) koff[i] = kOutOfRange;
+        if (8 * v_kc >= key_lim) voff[i] = kOutOfRange;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = v_d0 + 32 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key0 + 8 * v_kc < nkeys) {
-        int slot, n;
-        locate(8 * v_kc, slot, n);
-        v = *(const u32x4*)(vbase + slot * a.slot_elems + (int64_t)d * N + n);
-      }
-      vst[i] = v;
-    }
+    for (int i = 0; i < 4; ++i) kst[i] = bload(krs, koff[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vst[i] = bload(vrs, voff[i]);
     // advance the cursor by one tile
     cur_n += kBlockN;
     while (cur_n >= N) {
@@ -164,9 +220,11 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-  float m_run = -1.0e30f;  // running max of scaled scores (log2 units)
-  float l_run = 0.0f;      // this lane's partial row sum (its 16-key halves)
+  float m_run = -1.0e30f;  // running row max of scaled scores (log2 units), maybe stale by < 8
+  float l_run = 0.0f;      // this lane's partial row sum of the bf16 weights
   const float cl = a.c_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const f32x16 zero16 = {};
 
   // A-operand row m of the score MFMA reads key kappa(m): lane half hf of
   // output register i then holds key 16*hf + i of each 32-key block.
@@ -185,9 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
     const uint16_t* Vl = Kl + kKTile;
 
     // S^T = K Q^T for keys [0,32) and [32,64) of the tile
-    f32x16 s0, s1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { s0[i] = 0.0f; s1[i] = 0.0f; }
+    f32x16 s0 = zero16, s1 = zero16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 k0 = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
@@ -197,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
     }
 
     // mask keys past the end (last tile only)
-    const int key_lim = nkeys - kt * kBlockN;  // valid keys in this tile
+    const int key_lim = nkeys - kt * kBlockN;
     if (key_lim < kBlockN) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -206,41 +262,37 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
       }
     }
 
-    // online softmax (log2 domain)
-    float mx = s0[0];
+    // online softmax (log2 domain); O and l are rescaled only when some row max
+    // grows past the stale one by more than 2^8 (wave-uniform decision)
+    float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+    for (int i = 2; i < 16; i += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s0[i + 1]));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * cl);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.0f;
+    for (int i = 0; i < 16; i += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
+    const float mt = xhalf_max(mx) * cl;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], cl, -m_new));
-      s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], cl, -m_new));
-      ls += s0[i] + s1[i];
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
-    l_run = l_run * alpha + ls;
+    const float neg_m = -m_run;
+    u32x4 pw[4];  // P^T operands: block b, half-step u -> keys 32b + 16hf + 8u + 0..7
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-
-    // P^T operands: block b, half-step u -> keys 32b + 16hf + 8u + 0..7
-    bf16x8 pb[4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4 w0, w1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16x2(s0[8 * u + 2 * e], s0[8 * u + 2 * e + 1]);
-        w1[e] = pack_bf16x2(s1[8 * u + 2 * e], s1[8 * u + 2 * e + 1]);
-      }
-      pb[u] = as_bf16x8(w0);
-      pb[2 + u] = as_bf16x8(w1);
+    for (int e = 0; e < 8; ++e) {
+      const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m));
+      const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m));
+      const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m));
+      const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m));
+      const uint32_t pa = pack2(a0, a1), pb = pack2(b0, b1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
+      pw[e >> 2][e & 3] = pa;
+      pw[2 + (e >> 2)][e & 3] = pb;
     }
 
     // O^T += V^T P^T
@@ -252,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u) {
           const bf16x8 vf =
               *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * b + 16 * hf + 8 * u);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[2 * b + u], o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw[2 * b + u]), o[dt], 0, 0, 0);
         }
       }
     }
@@ -262,8 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: O = O^T / l, bf16, token-major -----------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
+  const float inv = 1.0f / xhalf_sum(l_run);
   if (qvalid) {
     uint16_t* orow = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim;
 #pragma unroll
@@ -272,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
       for (int g4 = 0; g4 < 4; ++g4) {
         // registers 4*g4 .. 4*g4+3 hold dims 32dt + 8g4 + 4hf + 0..3
         u32x2 w;
-        w[0] = pack_bf16x2(o[dt][4 * g4 + 0] * inv, o[dt][4 * g4 + 1] * inv);
-        w[1] = pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+        w[0] = pack2(o[dt][4 * g4 + 0] * inv, o[dt][4 * g4 + 1] * inv);
+        w[1] = pack2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
         *(u32x2*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
       }
     }
@@ -281,12 +332,18 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
 }
 
 hipError_t prepare_window_attn() {
-  return hipFuncSetAttribute((const void*)window_attn_kernel,
+  hipError_t e = hipFuncSetAttribute((const void*)window_attn_kernel<false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)window_attn_kernel<true>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
 }
 
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(window_attn_kernel, dim3((unsigned)a.total_tiles), dim3(kThreads), kLdsBytes, s, a);
+  if (a.N < kBlockN)
+    hipLaunchKernelGGL(window_attn_kernel<true>, dim3((unsigned)a.total_tiles), dim3(kThreads), kLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL(window_attn_kernel<false>, dim3((unsigned)a.total_tiles), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
