@@ -8,22 +8,27 @@
 // passes are batched ("Optimizing Real-Time Video Generation on Trainium
 // Chips", section 8) -- here as several query segments in one grid.
 //
-// Work decomposition: one work-group = (segment, head, 128 query rows), four
-// waves of 32 query rows each.  Per 64-key tile:
-//   S^T[key][q] = K_tile . Q^T      v_mfma_f32_32x32x16_bf16, 2 tiles x 8 k-steps
+// Work decomposition.  One work-group = (segment, head, 256 query rows):
+// four waves (one per SIMD), each owning two groups of 32 query rows.  Per
+// 64-key tile and group:
+//   S^T[key][q] = K_tile . Q^T    2 key blocks x 8 k-steps of v_mfma_f32_32x32x16_bf16
 //   online softmax in float32, exp2 with scale*log2(e) folded into one FMA
-//   O^T[d][q]  += V^T_tile . P^T    4 dim tiles x 4 k-steps
+//   O^T[d][q]  += V^T_tile . P^T  4 dim blocks x 4 k-steps
+// Every K and V fragment read from LDS feeds the MFMAs of both groups.
 // Computing the transposed products puts one query per lane (lane % 32) in
-// both accumulators, so the row max needs one cross-half exchange, the row
-// sum none until the end, and the rescale is a per-lane scalar.  The key
-// order inside a tile is permuted (kappa below) so that each lane's 16
-// softmax values are 16 consecutive keys, which is what the P^T operand of
-// the value product needs; the softmax is order-free over keys.
+// both accumulators, so a row max needs one cross-half exchange, the row sum
+// none until the end, and the rescale is a per-lane scalar.  The key order
+// inside a tile is permuted (kappa below) so that each lane's 16 softmax
+// values per key block are 16 consecutive keys, which is what the P^T
+// operand of the value product needs; the softmax is order-free over keys.
 //
-// K/V tiles are gathered from ring slots (a tile may straddle frames), staged
-// through LDS with register prefetch of the next tile, two LDS buffers and
-// one barrier per tile.  Q is loaded once per work-group with 3D-RoPE applied
-// on the fly (bit-identical to rf_rope3d_apply); keys are stored rotated.
+// Software pipeline per wave, iteration j: the score MFMAs of tile j are
+// issued alongside the softmax of tile j-1, then the value MFMAs of tile j-1
+// alongside staging the next K/V tiles.  K/V tiles are gathered from the
+// ring slots (a tile may straddle two frames) with raw buffer loads into
+// registers and written to LDS one iteration later; the K pipeline runs one
+// tile ahead of the V pipeline.  Q is loaded once with 3D-RoPE applied on
+// the fly (bit-identical to rf_rope3d_apply); keys are stored rotated.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,15 +40,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlockM = 128;               // query rows per work-group
+constexpr int kGroups = 2;                 // 32-query groups per wave (share every K/V fragment)
+constexpr int kWaves = 4;                  // one wave per SIMD
+constexpr int kBlockM = kWaves * kGroups * 32;  // query rows per work-group (256)
 constexpr int kBlockN = 64;                // keys per tile
-constexpr int kThreads = 256;              // 4 waves
+constexpr int kThreads = kWaves * 64;
 constexpr int kKRow = kHeadDim + 8;        // LDS row stride of K tile (272 B: conflict-free 16 B reads)
 constexpr int kVRow = kBlockN + 8;         // LDS row stride of V^T tile (144 B)
 constexpr int kKTile = kBlockN * kKRow;    // elements
 constexpr int kVTile = kHeadDim * kVRow;   // elements
-constexpr int kStage = kKTile + kVTile;    // one LDS buffer, elements
-constexpr size_t kLdsBytes = 2 * kStage * sizeof(uint16_t);
+constexpr size_t kLdsBytes = 2 * (kKTile + kVTile) * sizeof(uint16_t);  // K and V, two each
 constexpr float kRescaleLog2 = 8.0f;       // rescale O only when a row max grows by > 2^8
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // buffer offset past the end: the load returns 0
@@ -91,7 +97,7 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
 // general per-row frame walk is used.  Otherwise a tile straddles at most one
 // frame boundary and each row picks one of two bases.
 template <bool kSmallN>
-__global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -110,28 +116,35 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   const int h = local / sg.q_tiles;
   const int qt = local - h * sg.q_tiles;
 
-  // ---- Q fragment, RoPE'd on load: lane holds query row lr, dims 16s+8hf..+7 --
-  const int qi = qt * kBlockM + wave * 32 + lr;
-  const bool qvalid = qi < sg.q_tokens;
-  bf16x8 qf[8];
-  if (qvalid) {
-    const int f = qi / a.N;
-    const int pin = qi - f * a.N;
-    const int row = pin / a.gw;
-    const int col = pin - row * a.gw;
-    const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;
+  // ---- Q fragments, RoPE'd on load: group g of this wave holds query rows
+  // q0 + 32g + lr; lane half hf holds dims 16s + 8hf .. +7 of k-step s ------
+  const int q0 = qt * kBlockM + wave * (kGroups * 32);
+  bf16x8 qf[kGroups][8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hf;
-      u32x4 x = *(const u32x4*)(qrow + 8 * c);
-      qf[s] = as_bf16x8(rope_chunk(x, 4 * c, sg.q_t0 + f, row, col, a.tab));
+  for (int g = 0; g < kGroups; ++g) {
+    const int qi = q0 + 32 * g + lr;
+    if (qi < sg.q_tokens) {
+      const int f = qi / a.N;
+      const int pin = qi - f * a.N;
+      const int row = pin / a.gw;
+      const int col = pin - row * a.gw;
+      const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + hf;
+        u32x4 x = *(const u32x4*)(qrow + 8 * c);
+        qf[g][s] = as_bf16x8(rope_chunk(x, 4 * c, sg.q_t0 + f, row, col, a.tab));
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[g][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
   // ---- tile loaders (byte offsets into the rings, raw buffer loads) ------------
+  // The K pipeline runs one tile ahead of the V pipeline: tile j's keys are
+  // needed in iteration j (scores), its values in iteration j+1 (after the
+  // softmax), so two LDS buffers per operand suffice.
   const int nkeys = sg.ctx_keys;
   const int ntiles = (nkeys + kBlockN - 1) / kBlockN;
   const int N = a.N;
@@ -149,79 +162,95 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   const int v_d0 = tid >> 3, v_kc = tid & 7;
   u32x4 kst[4], vst[4];
 
-  // Cursor of the tile start in the key stream (uniform): slot and token offset.
-  int cur_slot = sg.ctx_slot0;
-  int cur_n = 0;
+  // Cursors of the next tile to load (uniform): slot and token offset of its first key.
+  int kslot = sg.ctx_slot0, kn = 0, kload = 0;
+  int vslot = sg.ctx_slot0, vn = 0, vload = 0;
+  auto advance = [&](int& slot, int& n) {
+    n += kBlockN;
+    while (n >= N) {
+      n -= N;
+      slot = (slot + 1 == W) ? 0 : slot + 1;
+    }
+  };
 
-  auto load_tile = [&](int kt) {
-    const int key_lim = nkeys - kt * kBlockN;  // valid keys in this tile
-    uint32_t koff[4], voff[4];
+  auto load_k = [&]() {
+    const int key_lim = nkeys - kload * kBlockN;  // valid keys in this tile (may be <= 0)
+    uint32_t off[4];
     if constexpr (!kSmallN) {
-      const int b = N - cur_n;  // keys of this tile still in the current frame
-      const int nxt = (cur_slot + 1 == W) ? 0 : cur_slot + 1;
-      const uint32_t ka = (uint32_t)cur_slot * slot_b + k_head + (uint32_t)cur_n * (kHeadDim * 2u);
+      const int b = N - kn;  // keys of this tile still in the current frame
+      const int nxt = (kslot + 1 == W) ? 0 : kslot + 1;
+      const uint32_t ka = (uint32_t)kslot * slot_b + k_head + (uint32_t)kn * (kHeadDim * 2u);
       const uint32_t kb = (uint32_t)nxt * slot_b + k_head - (uint32_t)b * (kHeadDim * 2u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = k_r0 + 16 * i;
-        koff[i] = (uint32_t)r * (kHeadDim * 2u) + 16u * k_c + (r < b ? ka : kb);
+        off[i] = (uint32_t)r * (kHeadDim * 2u) + 16u * k_c + (r < b ? ka : kb);
       }
-      const uint32_t vbase = (8 * v_kc < b)
-                                 ? (uint32_t)cur_slot * slot_b + v_head + (uint32_t)cur_n * 2u
-                                 : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        voff[i] = vbase + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u + 16u * v_kc;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int n = cur_n + k_r0 + 16 * i, slot = cur_slot;
+        int n = kn + k_r0 + 16 * i, slot = kslot;
         while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
-        koff[i] = (uint32_t)slot * slot_b + k_head + (uint32_t)n * (kHeadDim * 2u) + 16u * k_c;
-      }
-      int n = cur_n + 8 * v_kc, slot = cur_slot;
-      while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        voff[i] = (uint32_t)slot * slot_b + v_head + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u +
-                  (uint32_t)n * 2u;
-    }
-    if (key_lim < kBlockN) {  // last tile: keys past the end read as zeros
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (k_r0 + 16 * i >= key_lim) koff[i] = kOutOfRange;
-        if (8 * v_kc >= key_lim) voff[i] = kOutOfRange;
+        off[i] = (uint32_t)slot * slot_b + k_head + (uint32_t)n * (kHeadDim * 2u) + 16u * k_c;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kst[i] = bload(krs, koff[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vst[i] = bload(vrs, voff[i]);
-    // advance the cursor by one tile
-    cur_n += kBlockN;
-    while (cur_n >= N) {
-      cur_n -= N;
-      cur_slot = (cur_slot + 1 == W) ? 0 : cur_slot + 1;
+    for (int i = 0; i < 4; ++i) {
+      if (k_r0 + 16 * i >= key_lim) off[i] = kOutOfRange;  // past the end: zeros
+      kst[i] = bload(krs, off[i]);
     }
+    advance(kslot, kn);
+    ++kload;
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* Kl = lds + buf * kStage;
-    uint16_t* Vl = Kl + kKTile;
+  auto load_v = [&]() {
+    const int key_lim = nkeys - vload * kBlockN;
+    uint32_t base;
+    if constexpr (!kSmallN) {
+      const int b = N - vn;
+      const int nxt = (vslot + 1 == W) ? 0 : vslot + 1;
+      base = (8 * v_kc < b) ? (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u
+                            : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
+    } else {
+      int n = vn + 8 * v_kc, slot = vslot;
+      while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
+      base = (uint32_t)slot * slot_b + v_head + (uint32_t)n * 2u - 16u * v_kc;
+    }
+    const bool valid = 8 * v_kc < key_lim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = base + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u + 16u * v_kc;
+      vst[i] = bload(vrs, valid ? off : kOutOfRange);
+    }
+    advance(vslot, vn);
+    ++vload;
+  };
+
+  auto store_k = [&](int buf) {
+    uint16_t* Kl = lds + buf * kKTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(u32x4*)(Kl + (k_r0 + 16 * i) * kKRow + 8 * k_c) = kst[i];
+  };
+  auto store_v = [&](int buf) {
+    uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(u32x4*)(Vl + (v_d0 + 32 * i) * kVRow + 8 * v_kc) = vst[i];
   };
 
   // ---- running state -----------------------------------------------------------
-  f32x16 o[4];
+  f32x16 o[kGroups][4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int g = 0; g < kGroups; ++g)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-  float m_run = -1.0e30f;  // running row max of scaled scores (log2 units), maybe stale by < 8
-  float l_run = 0.0f;      // this lane's partial row sum of the bf16 weights
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.0f;
+  float m_run[kGroups], l_run[kGroups];  // running row max (log2 units, stale by < 8), row sum
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    m_run[g] = -1.0e30f;
+    l_run[g] = 0.0f;
+  }
   const float cl = a.c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16 zero16 = {};
@@ -230,72 +259,66 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
   // output register i then holds key 16*hf + i of each 32-key block.
   const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_tile(kt + 1);
-
-    const uint16_t* Kl = lds + buf * kStage;
-    const uint16_t* Vl = Kl + kKTile;
-
-    // S^T = K Q^T for keys [0,32) and [32,64) of the tile
-    f32x16 s0 = zero16, s1 = zero16;
+  // S^T = K Q^T, keys [0,32) and [32,64) of the tile in K buffer `buf`, for
+  // both query groups; every K fragment read from LDS feeds two MFMAs.
+  auto scores = [&](int buf, f32x16 (&S)[kGroups][2]) {
+    const uint16_t* Kl = lds + buf * kKTile;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) S[g][0] = S[g][1] = zero16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 k0 = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
       const bf16x8 k1 = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
-    }
-
-    // mask keys past the end (last tile only)
-    const int key_lim = nkeys - kt * kBlockN;
-    if (key_lim < kBlockN) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (16 * hf + i >= key_lim) s0[i] = -INFINITY;
-        if (32 + 16 * hf + i >= key_lim) s1[i] = -INFINITY;
+      for (int g = 0; g < kGroups; ++g) {
+        S[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[g][s], S[g][0], 0, 0, 0);
+        S[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[g][s], S[g][1], 0, 0, 0);
       }
     }
+  };
 
-    // online softmax (log2 domain); O and l are rescaled only when some row max
-    // grows past the stale one by more than 2^8 (wave-uniform decision)
+  // Online softmax of one group's tile scores (log2 domain) into bf16 weights
+  // pw.  The running max only moves when some row's tile max exceeds it by
+  // more than 2^8 (wave-uniform decision); alpha then rescales l here and O
+  // before the next value product.  The row sums are added separately.
+  auto softmax = [&](int g, f32x16& s0, f32x16& s1, uint32_t (&pr)[16], bool& rescale, float& alpha) {
     float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s0[i + 1]));
+    for (int i = 2; i < 16; i += 2)
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s0[i + 1]));
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
+    for (int i = 0; i < 16; i += 2)
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
     const float mt = xhalf_max(mx) * cl;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    }
-    const float neg_m = -m_run;
-    u32x4 pw[4];  // P^T operands: block b, half-step u -> keys 32b + 16hf + 8u + 0..7
+    rescale = __builtin_amdgcn_ballot_w64(mt > m_run[g] + kRescaleLog2) != 0;
+    const float m_new = rescale ? fmaxf(m_run[g], mt) : m_run[g];
+    alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+    m_run[g] = m_new;
+    l_run[g] *= alpha;
+    const float neg_m = -m_new;
+    // pr[e]: keys 2e, 2e+1 of this lane's 16 in block 0; pr[8+e]: same in block 1
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m));
-      const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m));
-      const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m));
-      const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m));
-      const uint32_t pa = pack2(a0, a1), pb = pack2(b0, b1);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
-      pw[e >> 2][e & 3] = pa;
-      pw[2 + (e >> 2)][e & 3] = pb;
+      pr[e] = pack2(__builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m)),
+                    __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m)));
+      pr[8 + e] = pack2(__builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m)),
+                        __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m)));
     }
+  };
 
-    // O^T += V^T P^T
+  // Row sums of the bf16 weights.  They are read from the scalar words: the
+  // compiler picks wrong registers for bf16x2 bit-casts of elements of a
+  // 4-word vector feeding the dot2 builtin.
+  auto row_sums = [&](int g, const uint32_t (&pr)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[i]), ones, l_run[g], false);
+  };
+
+  // O^T += V^T P^T with the values in V buffer `buf`, both groups per fragment.
+  // P^T operand of block b, half-step u: keys 32b + 16hf + 8u + 0..7.
+  auto values = [&](int buf, const uint32_t (&pr)[kGroups][16]) {
+    const uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -304,28 +327,118 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u) {
           const bf16x8 vf =
               *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * b + 16 * hf + 8 * u);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw[2 * b + u]), o[dt], 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            const int w = 8 * b + 4 * u;
+            const u32x4 pv = {pr[g][w], pr[g][w + 1], pr[g][w + 2], pr[g][w + 3]};
+            o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pv), o[g][dt], 0, 0, 0);
+          }
         }
       }
     }
+  };
 
-    if (more) store_tile(buf ^ 1);
+  auto rescale_o = [&](int g, bool rescale, float alpha) {
+    if (rescale) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+    }
+  };
+
+  // Keeps values materialised at this point (no instruction is emitted): the
+  // softmax stays in the phase whose MFMAs it is meant to overlap.
+  auto pin = [](const uint32_t (&pr)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(pr[i]));
+  };
+
+  // ---- software pipeline over key tiles ----------------------------------------
+  // iteration j, phase 1: scores of tile j   | softmax of tile j-1
+  //              phase 2: values of tile j-1 | stage K_{j+1}, V_j to LDS,
+  //                                            fetch K_{j+2}, V_{j+1}
+  load_k();  // K_0
+  load_v();  // V_0
+  store_k(0);
+  store_v(0);
+  load_k();  // K_1
+  __syncthreads();
+  f32x16 sp[kGroups][2];  // scores of the previous tile
+  scores(0, sp);
+  store_k(1);
+  load_k();  // K_2
+  load_v();  // V_1
+  __syncthreads();
+
+  for (int j = 1; j < ntiles; ++j) {
+    f32x16 sn[kGroups][2];
+    uint32_t pw[kGroups][16];
+    bool rs[kGroups];
+    float alpha[kGroups];
+    scores(j & 1, sn);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      softmax(g, sp[g][0], sp[g][1], pw[g], rs[g], alpha[g]);
+      pin(pw[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) rescale_o(g, rs[g], alpha[g]);
+    values((j - 1) & 1, pw);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) row_sums(g, pw[g]);
+    store_k((j + 1) & 1);  // K_{j+1}
+    store_v(j & 1);        // V_j
+    load_k();              // K_{j+2}
+    load_v();              // V_{j+1}
     __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      sp[g][0] = sn[g][0];
+      sp[g][1] = sn[g][1];
+    }
+  }
+
+  {  // last tile: mask keys past the end, then its softmax and values
+    const int key_lim = nkeys - (ntiles - 1) * kBlockN;
+    if (key_lim < kBlockN) {
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (16 * hf + i >= key_lim) sp[g][0][i] = -INFINITY;
+          if (32 + 16 * hf + i >= key_lim) sp[g][1][i] = -INFINITY;
+        }
+    }
+    uint32_t pw[kGroups][16];
+    bool rs[kGroups];
+    float alpha[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) softmax(g, sp[g][0], sp[g][1], pw[g], rs[g], alpha[g]);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) rescale_o(g, rs[g], alpha[g]);
+    values((ntiles - 1) & 1, pw);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) row_sums(g, pw[g]);
   }
 
   // ---- epilogue: O = O^T / l, bf16, token-major -----------------------------------
-  const float inv = 1.0f / xhalf_sum(l_run);
-  if (qvalid) {
-    uint16_t* orow = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+  for (int g = 0; g < kGroups; ++g) {
+    const float inv = 1.0f / xhalf_sum(l_run[g]);
+    const int qi = q0 + 32 * g + lr;
+    if (qi < sg.q_tokens) {
+      uint16_t* orow = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // registers 4*g4 .. 4*g4+3 hold dims 32dt + 8g4 + 4hf + 0..3
-        u32x2 w;
-        w[0] = pack2(o[dt][4 * g4 + 0] * inv, o[dt][4 * g4 + 1] * inv);
-        w[1] = pack2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
-        *(u32x2*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          // registers 4*g4 .. 4*g4+3 hold dims 32dt + 8g4 + 4hf + 0..3
+          u32x2 w;
+          w[0] = pack2(o[g][dt][4 * g4 + 0] * inv, o[g][dt][4 * g4 + 1] * inv);
+          w[1] = pack2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
+          *(u32x2*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
+        }
       }
     }
   }
