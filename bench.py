@@ -267,10 +267,14 @@ def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
                                       rows=rows, block=64, workers=workers)
         return o, time.perf_counter() - t0
 
+    # two probes separate the fixed cost (rotating the context keys) from the
+    # per-row cost; then size the sample for about `cpu_seconds` of oracle time
     rng = np.random.default_rng(0)
-    probe_rows = np.sort(rng.choice(15 * N, 64, replace=False))
-    _, t_probe = run(probe_rows)
-    n_rows = int(np.clip(64 * args.cpu_seconds / max(t_probe, 1e-3), 64, 4096))
+    _, t_a = run(np.sort(rng.choice(15 * N, 64, replace=False)))
+    _, t_b = run(np.sort(rng.choice(15 * N, 576, replace=False)))
+    per_row = max((t_b - t_a) / 512.0, 1e-6)
+    fixed = max(t_a - 64 * per_row, 0.0)
+    n_rows = int(np.clip((args.cpu_seconds - fixed) / per_row, 64, 15 * N))
     rows = np.sort(rng.choice(15 * N, n_rows, replace=False))
     o, secs = run(rows)
     flops = 4.0 * n_rows * lk * H * D
