@@ -24,8 +24,10 @@ using namespace rfattn;
 struct rf_ctx {
   rf_geom g;
   int device;
-  float2* d_tab;  // one allocation: [t table | h table | w table]
+  float2* d_tab;      // one allocation: [t table | h table | w table]
   RopeTables tab;
+  int max_workers;    // persistent attention work-groups: kWorkersPerCu per CU
+  float* d_partial;   // attention workspace: 2 * max_workers partial results
 };
 
 namespace {
@@ -153,19 +155,25 @@ rf_status rf_create(const rf_geom* g, rf_ctx** out) {
   fill_axis(host, g->grid_w, g->rope_pairs[2], g->rope_base);
   if (host.empty()) host.push_back(make_float2(1.f, 0.f));
 
+  const int max_workers = kWorkersPerCu * prop.multiProcessorCount;
   float2* d = nullptr;
+  float* part = nullptr;
   e = hipMalloc((void**)&d, host.size() * sizeof(float2));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(tables)");
-  e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
+  e = hipMalloc((void**)&part, (size_t)2 * max_workers * kPartFloats * sizeof(float));
+  if (e == hipSuccess) e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = prepare_window_attn();
   if (e != hipSuccess) {
     (void)hipFree(d);
-    return hip_fail(e, "table upload / kernel setup");
+    if (part) (void)hipFree(part);
+    return hip_fail(e, "table upload / workspace / kernel setup");
   }
   rf_ctx* c = new rf_ctx;
   c->g = *g;
   c->device = dev;
   c->d_tab = d;
+  c->max_workers = max_workers;
+  c->d_partial = part;
   c->tab.t = d;
   c->tab.h = d + off_h;
   c->tab.w = d + off_w;
@@ -179,6 +187,7 @@ rf_status rf_create(const rf_geom* g, rf_ctx** out) {
 void rf_destroy(rf_ctx* ctx) {
   if (!ctx) return;
   (void)hipFree(ctx->d_tab);
+  (void)hipFree(ctx->d_partial);
   delete ctx;
 }
 
@@ -300,10 +309,9 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   const rf_geom& g = ctx->g;
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
   const int64_t row = (int64_t)g.n_heads * g.head_dim;
-  const int bm = window_attn_block_m();
   AttnArgs a;
   std::memset(&a, 0, sizeof(a));
-  int64_t tiles = 0;
+  int64_t units = 0, tiles = 0;
   for (int i = 0; i < n_segs; ++i) {
     const rf_attn_segment& s = segs[i];
     if ((st = check_tensor(s.q, s.q_ld, row, "q")) != RF_OK) return st;
@@ -323,15 +331,32 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
     d.o_ld = s.o_ld;
     d.q_t0 = s.q_t0;
     d.q_tokens = (int)(s.q_frames * N);
-    d.q_tiles = (int)((d.q_tokens + bm - 1) / bm);
-    d.tile_begin = (int)tiles;
+    d.q_tiles = (d.q_tokens + kAttnBlockM - 1) / kAttnBlockM;
     d.ctx_keys = (int)(s.ctx_frames * N);
     d.ctx_slot0 = (int)mod(s.ctx_t0, c->capacity);
+    d.key_tiles = (d.ctx_keys + kAttnBlockN - 1) / kAttnBlockN;
+    d.tile_begin = (int)tiles;
+    d.unit_begin = (uint32_t)units;
     tiles += (int64_t)d.q_tiles * g.n_heads;
-    if (tiles > (int64_t(1) << 30)) return fail(RF_ERR_SHAPE, "grid too large");
+    units += (int64_t)d.q_tiles * g.n_heads * d.key_tiles;
+    if (units > (int64_t(1) << 31)) return fail(RF_ERR_SHAPE, "launch too large");
   }
+  a.total_units = (uint32_t)units;
+  // Whole rounds of tiles run one per work-group; the remainder is split.
+  const int64_t slots = ctx->max_workers;
+  a.dp_tiles = (int)(tiles / slots * slots);
+  int64_t sk_begin = 0;
+  for (int i = 0; i < n_segs; ++i) {  // unit index of tile dp_tiles
+    const SegDev& d = a.seg[i];
+    const int64_t seg_tiles = (int64_t)d.q_tiles * g.n_heads;
+    if (a.dp_tiles >= d.tile_begin && a.dp_tiles < d.tile_begin + seg_tiles)
+      sk_begin = d.unit_begin + (int64_t)(a.dp_tiles - d.tile_begin) * d.key_tiles;
+  }
+  if (a.dp_tiles == tiles) sk_begin = units;
+  a.sk_unit_begin = (uint32_t)sk_begin;
+  a.n_workers = (int)std::min<int64_t>(slots, units - sk_begin);
+  a.partial = ctx->d_partial;
   a.n_segs = n_segs;
-  a.total_tiles = (int)tiles;
   a.k_ring = (const uint16_t*)c->k;
   a.v_ring = (const uint16_t*)c->v;
   a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;

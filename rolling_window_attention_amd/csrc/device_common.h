@@ -14,6 +14,7 @@
 namespace rfattn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // cos/sin tables, float2 = (cos, sin) of pos * base^(-j/P), rounded to float32.
 struct RopeTables {

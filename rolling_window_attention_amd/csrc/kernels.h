@@ -10,6 +10,12 @@ namespace rfattn {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxSegments = 8;
+constexpr int kAttnBlockM = 128;   // query rows per attention work item
+constexpr int kAttnBlockN = 64;    // keys per key tile (one work unit per key tile)
+constexpr int kWorkersPerCu = 2;   // persistent attention work-groups per CU
+// One partial result of a split query tile: O [rows][head_dim], m [rows], l [rows].
+constexpr int kPartRows = kAttnBlockM;
+constexpr int kPartFloats = kPartRows * kHeadDim + 2 * kPartRows;
 
 struct RopeArgs {
   const uint16_t* x;
@@ -39,21 +45,27 @@ struct SegDev {
   int64_t q_ld, o_ld;
   int64_t q_t0;          // frame of the first query token
   int q_tokens;          // q_frames * N
-  int q_tiles;           // ceil(q_tokens / kBlockM)
-  int tile_begin;        // first work-group id of this segment
+  int q_tiles;           // ceil(q_tokens / kAttnBlockM)
   int ctx_keys;          // ctx_frames * N
   int ctx_slot0;         // ring slot of the first context frame
+  int key_tiles;         // ceil(ctx_keys / kAttnBlockN): work units per query tile
+  int tile_begin;        // first query tile of this segment (over all segments)
+  uint32_t unit_begin;   // first work unit of this segment
 };
 
 struct AttnArgs {
   SegDev seg[kMaxSegments];
   int n_segs;
-  int total_tiles;
+  uint32_t total_units;  // sum over segments of heads * q_tiles * key_tiles
+  int dp_tiles;          // tiles run whole, one work-group each (full rounds)
+  uint32_t sk_unit_begin;  // first unit of the split tiles (= unit of tile dp_tiles)
+  int n_workers;         // work-groups sharing the split tiles' units (0: none)
   const uint16_t* k_ring;
   const uint16_t* v_ring;
   int64_t slot_elems;
   int W, N, gw, H;
   float c_log2;          // scale * log2(e)
+  float* partial;        // workspace: 2 * n_workers partial results of kPartFloats
   RopeTables tab;
 };
 
@@ -61,6 +73,5 @@ hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s);
 hipError_t launch_roll(const RollArgs& a, hipStream_t s);
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 hipError_t prepare_window_attn();  // once per device, before the first launch
-int window_attn_block_m();
 
 }  // namespace rfattn

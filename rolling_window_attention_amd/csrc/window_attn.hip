@@ -6,15 +6,25 @@
 // paragraph); attention transposes live inside the attention kernel
 // (vibeleaderboard digest, key takeaways); the denoise and cache-update
 // passes are batched ("Optimizing Real-Time Video Generation on Trainium
-// Chips", section 8) -- here as several query segments in one grid.
+// Chips", section 8) -- here as several query segments in one launch.
 //
-// Work decomposition.  One work-group = (segment, head, 256 query rows):
-// four waves (one per SIMD), each owning two groups of 32 query rows.  Per
-// 64-key tile and group:
-//   S^T[key][q] = K_tile . Q^T    2 key blocks x 8 k-steps of v_mfma_f32_32x32x16_bf16
+// Work split.  A launch's query tiles -- (segment, head, 128 query rows) --
+// fill whole rounds of the GPU's work-group slots (two per CU) in the
+// ordinary way: one work-group per tile, numbered so that each XCD walks
+// consecutive tiles of one head and its resident work-groups read the same
+// K/V tiles at about the same time (L2 reuse).  The tiles left over for a
+// last, partly filled round are not run one per work-group: their key tiles
+// (64 keys each) are dealt out as equal contiguous ranges to one work-group
+// per slot (stream-K style), so the last round takes only the time its work
+// needs.  A tile cut by a range boundary leaves one partial result
+// (unnormalised O, running max, row sum) per piece in the workspace, and
+// window_attn_fixup merges the pieces.  A launch with fewer tiles than slots
+// (the cache-update pass alone) is split this way entirely.
+//
+// Per query tile: four waves of 32 query rows.  Per 64-key tile:
+//   S^T[key][q] = K_tile . Q^T      v_mfma_f32_32x32x16_bf16, 2 key blocks x 8 k-steps
 //   online softmax in float32, exp2 with scale*log2(e) folded into one FMA
-//   O^T[d][q]  += V^T_tile . P^T  4 dim blocks x 4 k-steps
-// Every K and V fragment read from LDS feeds the MFMAs of both groups.
+//   O^T[d][q]  += V^T_tile . P^T    4 dim blocks x 4 k-steps
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so a row max needs one cross-half exchange, the row sum
 // none until the end, and the rescale is a per-lane scalar.  The key order
@@ -23,12 +33,13 @@
 // operand of the value product needs; the softmax is order-free over keys.
 //
 // Software pipeline per wave, iteration j: the score MFMAs of tile j are
-// issued alongside the softmax of tile j-1, then the value MFMAs of tile j-1
-// alongside staging the next K/V tiles.  K/V tiles are gathered from the
+// issued next to the softmax of tile j-1, then the value MFMAs of tile j-1
+// next to staging the following K/V tiles.  K/V tiles are gathered from the
 // ring slots (a tile may straddle two frames) with raw buffer loads into
-// registers and written to LDS one iteration later; the K pipeline runs one
-// tile ahead of the V pipeline.  Q is loaded once with 3D-RoPE applied on
-// the fly (bit-identical to rf_rope3d_apply); keys are stored rotated.
+// registers and written to padded LDS rows one iteration later; the K
+// pipeline runs one tile ahead of the V pipeline.  Q is loaded with 3D-RoPE
+// applied on the fly (bit-identical to rf_rope3d_apply); keys are stored
+// rotated in the ring.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -40,11 +51,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kGroups = 2;                 // 32-query groups per wave (share every K/V fragment)
-constexpr int kWaves = 4;                  // one wave per SIMD
-constexpr int kBlockM = kWaves * kGroups * 32;  // query rows per work-group (256)
-constexpr int kBlockN = 64;                // keys per tile
-constexpr int kThreads = kWaves * 64;
+constexpr int kBlockM = kAttnBlockM;       // query rows per work item (128)
+constexpr int kBlockN = kAttnBlockN;       // keys per tile (64)
+constexpr int kThreads = 256;              // 4 waves
 constexpr int kKRow = kHeadDim + 8;        // LDS row stride of K tile (272 B: conflict-free 16 B reads)
 constexpr int kVRow = kBlockN + 8;         // LDS row stride of V^T tile (144 B)
 constexpr int kKTile = kBlockN * kKRow;    // elements
@@ -55,7 +64,6 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 fam
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // buffer offset past the end: the load returns 0
 constexpr int kXcds = 8;                   // MI355X: work-groups go round-robin over 8 XCDs
 
-int window_attn_block_m() { return kBlockM; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -93,52 +101,37 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return rem * per + (x - rem) * (per - 1) + idx;
 }
 
-// kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
-// general per-row frame walk is used.  Otherwise a tile straddles at most one
-// frame boundary and each row picks one of two bases.
+// One work item: query tile qt of head h of segment sg, key tiles [ka, kb).
+// A complete item (all key tiles) writes the normalised bf16 output; a piece
+// of a split tile writes its partial result to `part`.
 template <bool kSmallN>
-__global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+__device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const SegDev& sg,
+                                         int h, int qt, int ka, int kb, float* part) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lr = lane & 31;  // query column of this lane in the 32x32 tiles
   const int hf = lane >> 5;  // lane half: selects k-slots 0-7 / 8-15 of an MFMA step
 
-  // ---- work-group -> (segment, head, query tile) ---------------------------
-  const int tile = xcd_tile(blockIdx.x, a.total_tiles);
-  int si = 0;
+  // ---- Q fragment, RoPE'd on load: lane holds query row lr, dims 16s+8hf..+7 --
+  const int qi = qt * kBlockM + wave * 32 + lr;
+  const bool qvalid = qi < sg.q_tokens;
+  bf16x8 qf[8];
+  if (qvalid) {
+    const int f = qi / a.N;
+    const int pin = qi - f * a.N;
+    const int row = pin / a.gw;
+    const int col = pin - row * a.gw;
+    const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;
 #pragma unroll
-  for (int s = 1; s < kMaxSegments; ++s)
-    if (s < a.n_segs && tile >= a.seg[s].tile_begin) si = s;
-  const SegDev& sg = a.seg[si];
-  const int local = tile - sg.tile_begin;
-  const int h = local / sg.q_tiles;
-  const int qt = local - h * sg.q_tiles;
-
-  // ---- Q fragments, RoPE'd on load: group g of this wave holds query rows
-  // q0 + 32g + lr; lane half hf holds dims 16s + 8hf .. +7 of k-step s ------
-  const int q0 = qt * kBlockM + wave * (kGroups * 32);
-  bf16x8 qf[kGroups][8];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    const int qi = q0 + 32 * g + lr;
-    if (qi < sg.q_tokens) {
-      const int f = qi / a.N;
-      const int pin = qi - f * a.N;
-      const int row = pin / a.gw;
-      const int col = pin - row * a.gw;
-      const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = 2 * s + hf;
-        u32x4 x = *(const u32x4*)(qrow + 8 * c);
-        qf[g][s] = as_bf16x8(rope_chunk(x, 4 * c, sg.q_t0 + f, row, col, a.tab));
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qf[g][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < 8; ++s) {
+      const int c = 2 * s + hf;
+      u32x4 x = *(const u32x4*)(qrow + 8 * c);
+      qf[s] = as_bf16x8(rope_chunk(x, 4 * c, sg.q_t0 + f, row, col, a.tab));
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
   // ---- tile loaders (byte offsets into the rings, raw buffer loads) ------------
@@ -146,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   // needed in iteration j (scores), its values in iteration j+1 (after the
   // softmax), so two LDS buffers per operand suffice.
   const int nkeys = sg.ctx_keys;
-  const int ntiles = (nkeys + kBlockN - 1) / kBlockN;
+  const int ntiles = kb - ka;  // key tiles of this item: ka .. kb-1
   const int N = a.N;
   const int W = a.W;
   const uint32_t slot_b = (uint32_t)a.slot_elems * 2u;
@@ -162,9 +155,17 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   const int v_d0 = tid >> 3, v_kc = tid & 7;
   u32x4 kst[4], vst[4];
 
-  // Cursors of the next tile to load (uniform): slot and token offset of its first key.
-  int kslot = sg.ctx_slot0, kn = 0, kload = 0;
-  int vslot = sg.ctx_slot0, vn = 0, vload = 0;
+  // Cursors of the next tile to load (uniform): slot and token offset of its
+  // first key, starting at key tile ka.
+  int kslot, kn;
+  {
+    const int key0 = ka * kBlockN;
+    const int f0 = key0 / N;
+    kn = key0 - f0 * N;
+    kslot = (sg.ctx_slot0 + f0) % W;
+  }
+  int kload = ka;
+  int vslot = kslot, vn = kn, vload = ka;
   auto advance = [&](int& slot, int& n) {
     n += kBlockN;
     while (n >= N) {
@@ -238,19 +239,13 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   };
 
   // ---- running state -----------------------------------------------------------
-  f32x16 o[kGroups][4];
+  f32x16 o[4];
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.0f;
-  float m_run[kGroups], l_run[kGroups];  // running row max (log2 units, stale by < 8), row sum
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    m_run[g] = -1.0e30f;
-    l_run[g] = 0.0f;
-  }
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m_run = -1.0e30f;  // running row max of scaled scores (log2 units), maybe stale by < 8
+  float l_run = 0.0f;      // this lane's partial row sum of the bf16 weights
   const float cl = a.c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16 zero16 = {};
@@ -259,29 +254,24 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   // output register i then holds key 16*hf + i of each 32-key block.
   const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
 
-  // S^T = K Q^T, keys [0,32) and [32,64) of the tile in K buffer `buf`, for
-  // both query groups; every K fragment read from LDS feeds two MFMAs.
-  auto scores = [&](int buf, f32x16 (&S)[kGroups][2]) {
+  // S^T = K Q^T for keys [0,32) and [32,64) of the tile in K buffer `buf`
+  auto scores = [&](int buf, f32x16& s0, f32x16& s1) {
     const uint16_t* Kl = lds + buf * kKTile;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) S[g][0] = S[g][1] = zero16;
+    s0 = zero16;
+    s1 = zero16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 k0 = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
       const bf16x8 k1 = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        S[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[g][s], S[g][0], 0, 0, 0);
-        S[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[g][s], S[g][1], 0, 0, 0);
-      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }
   };
 
-  // Online softmax of one group's tile scores (log2 domain) into bf16 weights
-  // pw.  The running max only moves when some row's tile max exceeds it by
-  // more than 2^8 (wave-uniform decision); alpha then rescales l here and O
-  // before the next value product.  The row sums are added separately.
-  auto softmax = [&](int g, f32x16& s0, f32x16& s1, uint32_t (&pr)[16], bool& rescale, float& alpha) {
+  // Online softmax of one tile's scores (log2 domain) into bf16 weights pw.
+  // The running max only moves when some row's tile max exceeds it by more
+  // than 2^8 (wave-uniform decision); then alpha rescales l here and O later.
+  auto softmax = [&](f32x16& s0, f32x16& s1, u32x4 (&pw)[4], bool& rescale, float& alpha) {
     float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
 #pragma unroll
     for (int i = 2; i < 16; i += 2)
@@ -290,34 +280,28 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; i += 2)
       mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
     const float mt = xhalf_max(mx) * cl;
-    rescale = __builtin_amdgcn_ballot_w64(mt > m_run[g] + kRescaleLog2) != 0;
-    const float m_new = rescale ? fmaxf(m_run[g], mt) : m_run[g];
-    alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-    m_run[g] = m_new;
-    l_run[g] *= alpha;
+    rescale = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+    const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
     const float neg_m = -m_new;
-    // pr[e]: keys 2e, 2e+1 of this lane's 16 in block 0; pr[8+e]: same in block 1
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pr[e] = pack2(__builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m)),
-                    __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m)));
-      pr[8 + e] = pack2(__builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m)),
-                        __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m)));
+      const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m));
+      const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m));
+      const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m));
+      const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m));
+      const uint32_t pa = pack2(a0, a1), pb = pack2(b0, b1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
+      pw[e >> 2][e & 3] = pa;
+      pw[2 + (e >> 2)][e & 3] = pb;
     }
   };
 
-  // Row sums of the bf16 weights.  They are read from the scalar words: the
-  // compiler picks wrong registers for bf16x2 bit-casts of elements of a
-  // 4-word vector feeding the dot2 builtin.
-  auto row_sums = [&](int g, const uint32_t (&pr)[16]) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[i]), ones, l_run[g], false);
-  };
-
-  // O^T += V^T P^T with the values in V buffer `buf`, both groups per fragment.
-  // P^T operand of block b, half-step u: keys 32b + 16hf + 8u + 0..7.
-  auto values = [&](int buf, const uint32_t (&pr)[kGroups][16]) {
+  // O^T += V^T P^T with the values in V buffer `buf`
+  auto values = [&](int buf, const u32x4 (&pw)[4]) {
     const uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -327,107 +311,77 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u) {
           const bf16x8 vf =
               *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * b + 16 * hf + 8 * u);
-#pragma unroll
-          for (int g = 0; g < kGroups; ++g) {
-            const int w = 8 * b + 4 * u;
-            const u32x4 pv = {pr[g][w], pr[g][w + 1], pr[g][w + 2], pr[g][w + 3]};
-            o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pv), o[g][dt], 0, 0, 0);
-          }
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw[2 * b + u]), o[dt], 0, 0, 0);
         }
       }
     }
   };
 
-  auto rescale_o = [&](int g, bool rescale, float alpha) {
+  auto rescale_o = [&](bool rescale, float alpha) {
     if (rescale) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
   };
 
-  // Keeps values materialised at this point (no instruction is emitted): the
-  // softmax stays in the phase whose MFMAs it is meant to overlap.
-  auto pin = [](const uint32_t (&pr)[16]) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(pr[i]));
-  };
-
   // ---- software pipeline over key tiles ----------------------------------------
-  // iteration j, phase 1: scores of tile j   | softmax of tile j-1
-  //              phase 2: values of tile j-1 | stage K_{j+1}, V_j to LDS,
-  //                                            fetch K_{j+2}, V_{j+1}
+  // iteration j: scores of tile j | softmax of tile j-1 ; values of tile j-1 |
+  // stage K_{j+1} and V_j to LDS ; fetch K_{j+2} and V_{j+1} from the ring.
   load_k();  // K_0
   load_v();  // V_0
   store_k(0);
   store_v(0);
   load_k();  // K_1
   __syncthreads();
-  f32x16 sp[kGroups][2];  // scores of the previous tile
-  scores(0, sp);
+  f32x16 sp0, sp1;  // scores of the previous tile
+  scores(0, sp0, sp1);
   store_k(1);
   load_k();  // K_2
   load_v();  // V_1
   __syncthreads();
 
   for (int j = 1; j < ntiles; ++j) {
-    f32x16 sn[kGroups][2];
-    uint32_t pw[kGroups][16];
-    bool rs[kGroups];
-    float alpha[kGroups];
-    scores(j & 1, sn);
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      softmax(g, sp[g][0], sp[g][1], pw[g], rs[g], alpha[g]);
-      pin(pw[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) rescale_o(g, rs[g], alpha[g]);
+    f32x16 sn0, sn1;
+    u32x4 pw[4];
+    bool rs;
+    float alpha;
+    scores(j & 1, sn0, sn1);
+    softmax(sp0, sp1, pw, rs, alpha);
+    rescale_o(rs, alpha);
     values((j - 1) & 1, pw);
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) row_sums(g, pw[g]);
     store_k((j + 1) & 1);  // K_{j+1}
     store_v(j & 1);        // V_j
     load_k();              // K_{j+2}
     load_v();              // V_{j+1}
     __syncthreads();
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      sp[g][0] = sn[g][0];
-      sp[g][1] = sn[g][1];
-    }
+    sp0 = sn0;
+    sp1 = sn1;
   }
 
   {  // last tile: mask keys past the end, then its softmax and values
-    const int key_lim = nkeys - (ntiles - 1) * kBlockN;
+    const int key_lim = nkeys - (kb - 1) * kBlockN;
     if (key_lim < kBlockN) {
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (16 * hf + i >= key_lim) sp[g][0][i] = -INFINITY;
-          if (32 + 16 * hf + i >= key_lim) sp[g][1][i] = -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        if (16 * hf + i >= key_lim) sp0[i] = -INFINITY;
+        if (32 + 16 * hf + i >= key_lim) sp1[i] = -INFINITY;
+      }
     }
-    uint32_t pw[kGroups][16];
-    bool rs[kGroups];
-    float alpha[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) softmax(g, sp[g][0], sp[g][1], pw[g], rs[g], alpha[g]);
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) rescale_o(g, rs[g], alpha[g]);
+    u32x4 pw[4];
+    bool rs;
+    float alpha;
+    softmax(sp0, sp1, pw, rs, alpha);
+    rescale_o(rs, alpha);
     values((ntiles - 1) & 1, pw);
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) row_sums(g, pw[g]);
   }
 
-  // ---- epilogue: O = O^T / l, bf16, token-major -----------------------------------
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    const float inv = 1.0f / xhalf_sum(l_run[g]);
-    const int qi = q0 + 32 * g + lr;
-    if (qi < sg.q_tokens) {
+  // ---- epilogue --------------------------------------------------------------------
+  const float l_tot = xhalf_sum(l_run);
+  if (ka == 0 && kb == sg.key_tiles) {  // whole item: O = O^T / l, bf16, token-major
+    const float inv = 1.0f / l_tot;
+    if (qvalid) {
       uint16_t* orow = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -435,12 +389,139 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
           // registers 4*g4 .. 4*g4+3 hold dims 32dt + 8g4 + 4hf + 0..3
           u32x2 w;
-          w[0] = pack2(o[g][dt][4 * g4 + 0] * inv, o[g][dt][4 * g4 + 1] * inv);
-          w[1] = pack2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
+          w[0] = pack2(o[dt][4 * g4 + 0] * inv, o[dt][4 * g4 + 1] * inv);
+          w[1] = pack2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
           *(u32x2*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
         }
       }
     }
+  } else {  // piece of a split tile: unnormalised O [row][dim], then m[row], l[row]
+    const int r = wave * 32 + lr;  // row inside the query tile
+    float* orow = part + r * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 w = {o[dt][4 * g4 + 0], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+        *(f32x4*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
+      }
+    if (hf == 0) {
+      part[kPartRows * kHeadDim + r] = m_run;
+      part[kPartRows * kHeadDim + kPartRows + r] = l_tot;
+    }
+  }
+}
+
+// The contiguous unit range [r0, r1) of worker v out of P over U units.
+__device__ __forceinline__ uint32_t range_start(uint32_t v, uint32_t U, uint32_t P) {
+  return (uint32_t)(((uint64_t)v * U) / P);
+}
+
+// Segment, query tile and key tile of unit u.
+__device__ __forceinline__ int unit_segment(const AttnArgs& a, uint32_t u) {
+  int si = 0;
+#pragma unroll
+  for (int s = 1; s < kMaxSegments; ++s)
+    if (s < a.n_segs && u >= a.seg[s].unit_begin) si = s;
+  return si;
+}
+
+// kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
+// general per-row frame walk is used.  Otherwise a tile straddles at most one
+// frame boundary and each row picks one of two bases.
+template <bool kSmallN>
+__global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  if ((int)blockIdx.x < a.dp_tiles) {
+    // whole query tiles, one per work-group, in XCD-contiguous order
+    const int tile = xcd_tile(blockIdx.x, a.dp_tiles);
+    const uint32_t u = (uint32_t)tile;  // tile index; segments are found by their first tile
+    int si = 0;
+#pragma unroll
+    for (int s = 1; s < kMaxSegments; ++s)
+      if (s < a.n_segs && u >= (uint32_t)a.seg[s].tile_begin) si = s;
+    const SegDev& sg = a.seg[si];
+    const int tl = tile - sg.tile_begin;
+    const int h = tl / sg.q_tiles;
+    run_item<kSmallN>(a, lds, sg, h, tl - h * sg.q_tiles, 0, sg.key_tiles, nullptr);
+    return;
+  }
+  // the remaining tiles: equal contiguous ranges of key-tile units per worker
+  const uint32_t P = (uint32_t)a.n_workers;
+  const uint32_t v = (uint32_t)xcd_tile(blockIdx.x - a.dp_tiles, a.n_workers);
+  const uint32_t span = a.total_units - a.sk_unit_begin;
+  const uint32_t r0 = a.sk_unit_begin + range_start(v, span, P);
+  const uint32_t r1 = a.sk_unit_begin + range_start(v + 1, span, P);
+  for (uint32_t u = r0; u < r1;) {
+    const int si = unit_segment(a, u);
+    const SegDev& sg = a.seg[si];
+    const uint32_t local = u - sg.unit_begin;
+    const int tl = (int)(local / (uint32_t)sg.key_tiles);
+    const int ka = (int)local - tl * sg.key_tiles;
+    const int kb = (int)min((uint32_t)sg.key_tiles, (uint32_t)ka + (r1 - u));
+    const int h = tl / sg.q_tiles;
+    const int qt = tl - h * sg.q_tiles;
+    float* part = a.partial + (size_t)(2 * v + (u == r0 ? 0 : 1)) * kPartFloats;
+    __syncthreads();  // the previous item's LDS reads are done
+    run_item<kSmallN>(a, lds, sg, h, qt, ka, kb, part);
+    u += (uint32_t)(kb - ka);
+  }
+}
+
+// Merge the pieces of the query tile whose key tiles start in worker v's
+// range and continue past it: worker v holds the first piece (in its slot 0
+// if the tile starts its range, else slot 1), the following workers the
+// next pieces (their slot 0).  O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i.
+__global__ __launch_bounds__(256) void window_attn_fixup(AttnArgs a) {
+  const uint32_t P = (uint32_t)a.n_workers;
+  const uint32_t span = a.total_units - a.sk_unit_begin;
+  const uint32_t v = blockIdx.x;
+  const uint32_t r0 = a.sk_unit_begin + range_start(v, span, P);
+  const uint32_t r1 = a.sk_unit_begin + range_start(v + 1, span, P);
+  const uint32_t last = r1 - 1;
+  const int si = unit_segment(a, last);
+  const SegDev& sg = a.seg[si];
+  const uint32_t tl = (last - sg.unit_begin) / (uint32_t)sg.key_tiles;
+  const uint32_t t0 = sg.unit_begin + tl * (uint32_t)sg.key_tiles;  // the tile's units [t0, t1)
+  const uint32_t t1 = t0 + (uint32_t)sg.key_tiles;
+  if (t0 < r0 || t1 <= r1) return;  // started in an earlier range, or not split
+  const int h = (int)tl / sg.q_tiles;
+  const int qt = (int)tl - h * sg.q_tiles;
+  const int r = threadIdx.x >> 1;           // row inside the query tile
+  const int d0 = (threadIdx.x & 1) * 64;    // half of the head dimension
+  const int qi = qt * kBlockM + r;
+  if (qi >= sg.q_tokens) return;
+
+  float M = -INFINITY;
+  for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
+    const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
+    M = fmaxf(M, p[kPartRows * kHeadDim + r]);
+  }
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0.0f;
+  float L = 0.0f;
+  for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
+    const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
+    const float sc = __builtin_amdgcn_exp2f(p[kPartRows * kHeadDim + r] - M);
+    L += sc * p[kPartRows * kHeadDim + kPartRows + r];
+    const float* orow = p + r * kHeadDim + d0;
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const f32x4 x = *(const f32x4*)(orow + i);
+      acc[i] += sc * x[0];
+      acc[i + 1] += sc * x[1];
+      acc[i + 2] += sc * x[2];
+      acc[i + 3] += sc * x[3];
+    }
+  }
+  const float inv = 1.0f / L;
+  uint16_t* out = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim + d0;
+#pragma unroll
+  for (int i = 0; i < 64; i += 8) {
+    u32x4 w = {pack2(acc[i] * inv, acc[i + 1] * inv), pack2(acc[i + 2] * inv, acc[i + 3] * inv),
+               pack2(acc[i + 4] * inv, acc[i + 5] * inv), pack2(acc[i + 6] * inv, acc[i + 7] * inv)};
+    *(u32x4*)(out + i) = w;
   }
 }
 
@@ -453,10 +534,14 @@ hipError_t prepare_window_attn() {
 }
 
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.dp_tiles + a.n_workers));
   if (a.N < kBlockN)
-    hipLaunchKernelGGL(window_attn_kernel<true>, dim3((unsigned)a.total_tiles), dim3(kThreads), kLdsBytes, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<true>, grid, dim3(kThreads), kLdsBytes, s, a);
   else
-    hipLaunchKernelGGL(window_attn_kernel<false>, dim3((unsigned)a.total_tiles), dim3(kThreads), kLdsBytes, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<false>, grid, dim3(kThreads), kLdsBytes, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_workers == 0) return e;
+  hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.n_workers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
