@@ -23,7 +23,8 @@
  * Conventions shared by every call:
  *   - Tensors are bf16 (raw 16-bit patterns) in device memory that the
  *     CALLER owns.  The library allocates device memory only in rf_create
- *     (the RoPE tables) and frees it in rf_destroy.
+ *     (the RoPE tables and the attention workspace) and frees it in
+ *     rf_destroy; no call allocates.
  *   - Calls are asynchronous and stream-ordered: work is enqueued on
  *     `stream` (a hipStream_t passed as void*; NULL = the default stream)
  *     and the call returns without synchronising.
@@ -72,14 +73,19 @@ typedef struct {
   int64_t max_frame;       /* frame indices 0..max_frame-1 are supported            */
 } rf_geom;
 
-/* Opaque context: the geometry plus the device-resident cos/sin tables (each
- * float64 libm cos/sin of pos*b^(-j/P), rounded to float32).  Immutable after
- * creation; one context may be used from several threads and streams. */
+/* Opaque context: the geometry, the device-resident cos/sin tables (each
+ * float64 libm cos/sin of pos*b^(-j/P), rounded to float32) and the
+ * attention workspace (partial results of query tiles split across
+ * work-groups: 2 x 2 x CUs x 66.5 KB, 68 MB on a 256-CU MI355X).  The tables
+ * are immutable after creation; rf_rope3d_apply and rf_kvcache_roll may use
+ * one context from several threads and streams.  rf_window_attention calls
+ * that share a context share its workspace and must be ordered (one stream,
+ * or synchronised); use one context per concurrent stream otherwise. */
 typedef struct rf_ctx rf_ctx;
 
-/* Validate `g`, check that the current HIP device is gfx950, and upload the
- * RoPE tables.  This is the library's only allocation.  *out is set only on
- * RF_OK.  Synchronous. */
+/* Validate `g`, check that the current HIP device is gfx950, upload the
+ * RoPE tables and allocate the attention workspace.  These are the library's
+ * only allocations.  *out is set only on RF_OK.  Synchronous. */
 rf_status rf_create(const rf_geom* g, rf_ctx** out);
 
 /* Free a context (NULL is ignored).  The caller must first make sure no work
@@ -205,6 +211,12 @@ typedef struct {
  * enter the value product as bf16.  scale == 0 means 1/sqrt(head_dim).
  * The context length is a runtime argument (whole frames); nothing is
  * recompiled or reallocated when it changes.
+ *
+ * Work split: query tiles of 128 rows run whole on the GPU's work-group
+ * slots in full rounds; the tiles of a last, partly filled round are cut
+ * along their keys into equal shares for all slots and merged by a second
+ * kernel on the same stream (the result does not depend on the split beyond
+ * float32 rounding; it is deterministic for a given launch shape).
  *
  * Errors: RF_ERR_NULL, RF_ERR_ALIGN, RF_ERR_SHAPE (n_segs outside
  * 1..RF_MAX_SEGMENTS, q_frames/ctx_frames < 1, ld too small), RF_ERR_RANGE
