@@ -29,17 +29,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_fl
 // float64 -> bf16, round to nearest even, taken directly (no double rounding).
 // The float32 conversion rounds to nearest even; that can only mislead the
 // second rounding when it lands exactly on a bf16 halfway point (low 16 bits
-// 0x8000) without being exact.  In that case the float32 pattern is nudged
-// one float32 ulp towards the true value before the float32 -> bf16 rounding.
-// Finite inputs only (NaN/Inf are not produced by the library's arithmetic
-// on finite bf16 inputs of moderate size).
+// 0x8000) without being exact.  In that case the float32 pattern is moved one
+// float32 ulp towards the true value before the float32 -> bf16 rounding.
+// Written without branches (selects only).  Finite inputs only (NaN/Inf are
+// not produced by the library's arithmetic on finite bf16 inputs).
 __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
-  float f = (float)y;
+  const float f = (float)y;
   uint32_t fb = __float_as_uint(f);
-  if ((fb & 0xFFFFu) == 0x8000u) {
-    double back = (double)f;
-    if (back != y) fb += (fabs(y) > fabs(back)) ? 1u : 0xFFFFFFFFu;
-  }
+  const double back = (double)f;
+  const bool fix = ((fb & 0xFFFFu) == 0x8000u) && (back != y);
+  const uint32_t step = (fabs(y) > fabs(back)) ? 1u : 0xFFFFFFFFu;
+  fb += fix ? step : 0u;
   return (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
 }
 

@@ -15,11 +15,14 @@
 namespace rfattn {
 
 // ---------------------------------------------------------------------------
-// rope3d: each work-group owns TOK consecutive tokens; its threads walk the
-// TOK*H*16 sixteen-byte chunks of those rows with a stride of the block size,
-// so loads and stores are fully coalesced 16-byte accesses.
+// rope3d: each work-group owns kRopeTok consecutive tokens; each thread takes
+// up to kRopeBatch of their 16-byte chunks (stride: the block size), issues
+// all loads before any store, then rotates and stores -- so a thread keeps
+// kRopeBatch loads in flight instead of waiting for each (in-place use makes
+// the compiler keep every store behind the load of its own chunk only).
 // ---------------------------------------------------------------------------
 constexpr int kRopeTok = 8;
+constexpr int kRopeBatch = 8;
 
 __global__ __launch_bounds__(256) void rope3d_kernel(RopeArgs a) {
   const uint32_t row_chunks = (uint32_t)a.H * 16u;  // 16-byte chunks per token row
@@ -28,26 +31,39 @@ __global__ __launch_bounds__(256) void rope3d_kernel(RopeArgs a) {
   const float inv_row = 1.0f / (float)row_chunks;
   const float inv_n = 1.0f / (float)a.N;
   const float inv_gw = 1.0f / (float)a.gw;
-  for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) {
-    uint32_t rem;
-    uint32_t tl = small_div(q, row_chunks, inv_row, &rem);
-    int64_t tok = tok0 + tl;
-    if (tok >= a.n_tokens) break;  // q only grows: later chunks are past the end too
-    uint32_t h = rem >> 4, c = rem & 15u;
-    uint32_t pin;
-    uint32_t f = small_div((uint32_t)tok, (uint32_t)a.N, inv_n, &pin);
-    uint32_t col;
-    uint32_t row = small_div(pin, (uint32_t)a.gw, inv_gw, &col);
-    const u32x4* src = (const u32x4*)(a.x + tok * a.x_ld + h * 128u + c * 8u);
-    u32x4 v = __builtin_nontemporal_load(src);
-    u32x4 y = rope_chunk(v, (int)c * 4, a.t0 + f, (int)row, (int)col, a.tab);
-    u32x4* dst = (u32x4*)(a.y + tok * a.y_ld + h * 128u + c * 8u);
-    __builtin_nontemporal_store(y, dst);
+  for (uint32_t q0 = threadIdx.x; q0 < total; q0 += kRopeBatch * blockDim.x) {
+    u32x4 v[kRopeBatch];
+    int64_t tok[kRopeBatch];
+    uint32_t hc[kRopeBatch];
+    bool ok[kRopeBatch];
+#pragma unroll
+    for (int i = 0; i < kRopeBatch; ++i) {
+      const uint32_t q = q0 + (uint32_t)i * blockDim.x;
+      uint32_t rem;
+      const uint32_t tl = small_div(q, row_chunks, inv_row, &rem);
+      tok[i] = tok0 + tl;
+      hc[i] = rem;  // head * 16 + chunk
+      ok[i] = q < total && tok[i] < a.n_tokens;
+      if (ok[i])
+        v[i] = __builtin_nontemporal_load((const u32x4*)(a.x + tok[i] * a.x_ld + (rem >> 4) * 128u + (rem & 15u) * 8u));
+    }
+#pragma unroll
+    for (int i = 0; i < kRopeBatch; ++i) {
+      if (!ok[i]) continue;
+      uint32_t pin;
+      const uint32_t f = small_div((uint32_t)tok[i], (uint32_t)a.N, inv_n, &pin);
+      uint32_t col;
+      const uint32_t row = small_div(pin, (uint32_t)a.gw, inv_gw, &col);
+      const uint32_t c = hc[i] & 15u;
+      const u32x4 y = rope_chunk(v[i], (int)c * 4, a.t0 + f, (int)row, (int)col, a.tab);
+      __builtin_nontemporal_store(y, (u32x4*)(a.y + tok[i] * a.y_ld + (hc[i] >> 4) * 128u + c * 8u));
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// roll: a thread owns an 8-token x 8-dim block of one (frame, head).
+// roll: a thread owns an 8-token x 8-dim block of one (frame, head) of the
+// keys (grid z = 0) or of the values (z = 1).
 // Keys: 8 rows of 16 bytes are read, rotated, written to K[slot][h][n][d].
 // Values: the 8x8 bf16 block is transposed in registers and written as 8
 // rows of 16 bytes to V[slot][h][d][n] -- the transpose costs no extra pass.
@@ -86,6 +102,7 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a) {
   const int fh = blockIdx.y;                // frame * H + head
   const int f = fh / a.H;
   const int h = fh - f * a.H;
+  const bool is_v = blockIdx.z != 0;        // z = 0: keys, z = 1: values
   if (g >= (uint32_t)(a.N >> 3)) return;
 
   int slot = a.slot0 + f;
@@ -94,32 +111,31 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a) {
 
   const uint32_t n0 = g * 8u;
   const int64_t in_tok0 = (int64_t)f * a.N + n0;
-  u32x4 kin[8], vin[8];
+  const uint16_t* src = is_v ? a.v_new : a.k_new;
+  const int64_t ld = is_v ? a.v_ld : a.k_ld;
+  u32x4 in[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t tok = in_tok0 + j;
-    kin[j] = __builtin_nontemporal_load((const u32x4*)(a.k_new + tok * a.k_ld + h * 128 + c * 8));
-    vin[j] = __builtin_nontemporal_load((const u32x4*)(a.v_new + tok * a.v_ld + h * 128 + c * 8));
-  }
+  for (int j = 0; j < 8; ++j)
+    in[j] = __builtin_nontemporal_load((const u32x4*)(src + (in_tok0 + j) * ld + h * 128 + c * 8));
 
-  // Keys: rotate at (t, row, col) and store head-major.
-  uint32_t row = n0 / (uint32_t)a.gw;  // one division per thread; columns advance below
-  uint32_t col = n0 - row * (uint32_t)a.gw;
-  uint16_t* kslot = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)h * a.N * 128;
+  if (!is_v) {
+    // Keys: rotate at (t, row, col) and store head-major.
+    uint32_t row = n0 / (uint32_t)a.gw;  // one division per thread; columns advance below
+    uint32_t col = n0 - row * (uint32_t)a.gw;
+    uint16_t* kslot = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)h * a.N * 128;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4 y = rope_chunk(kin[j], (int)c * 4, t, (int)row, (int)col, a.tab);
-    *(u32x4*)(kslot + (int64_t)(n0 + j) * 128 + c * 8) = y;
-    if (++col == (uint32_t)a.gw) { col = 0; ++row; }
-  }
-
-  // Values: transpose the 8x8 block, store [d][n].
-  u32x4 vt[8];
-  transpose8x8(vin, vt);
-  uint16_t* vslot = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * 128 * a.N;
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 y = rope_chunk(in[j], (int)c * 4, t, (int)row, (int)col, a.tab);
+      *(u32x4*)(kslot + (int64_t)(n0 + j) * 128 + c * 8) = y;
+      if (++col == (uint32_t)a.gw) { col = 0; ++row; }
+    }
+  } else {
+    // Values: transpose the 8x8 block, store [d][n].
+    u32x4 vt[8];
+    transpose8x8(in, vt);
+    uint16_t* vslot = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * 128 * a.N;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    *(u32x4*)(vslot + (int64_t)(c * 8 + i) * a.N + n0) = vt[i];
+    for (int i = 0; i < 8; ++i) *(u32x4*)(vslot + (int64_t)(c * 8 + i) * a.N + n0) = vt[i];
   }
 }
 
@@ -132,7 +148,7 @@ hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s) {
 hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
   const unsigned groups = (unsigned)(a.N / 8);
   const unsigned threads = ((groups + 7) / 8) * 128;  // 8-group blocks x 16 chunks
-  dim3 grid((threads + 255) / 256, (unsigned)(a.n_frames * a.H));
+  dim3 grid((threads + 255) / 256, (unsigned)(a.n_frames * a.H), 2);
   hipLaunchKernelGGL(roll_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
