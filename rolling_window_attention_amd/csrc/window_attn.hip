@@ -255,8 +255,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
 
   // S^T = K Q^T for keys [0,32) and [32,64) of the tile in K buffer `buf`
+  // Both MFMA blocks run at raised wave priority: while one wave of a SIMD
+  // issues its MFMAs, the other wave's softmax VALU work fills the gaps.
   auto scores = [&](int buf, f32x16& s0, f32x16& s1) {
     const uint16_t* Kl = lds + buf * kKTile;
+    __builtin_amdgcn_s_setprio(1);
     s0 = zero16;
     s1 = zero16;
 #pragma unroll
@@ -266,6 +269,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of one tile's scores (log2 domain) into bf16 weights pw.
@@ -303,6 +307,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   // O^T += V^T P^T with the values in V buffer `buf`
   auto values = [&](int buf, const u32x4 (&pw)[4]) {
     const uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -315,6 +320,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   auto rescale_o = [&](bool rescale, float alpha) {
