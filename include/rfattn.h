@@ -76,7 +76,7 @@ typedef struct {
 /* Opaque context: the geometry, the device-resident cos/sin tables (each
  * float64 libm cos/sin of pos*b^(-j/P), rounded to float32) and the
  * attention workspace (partial results of query tiles split across
- * work-groups: 2 x 2 x CUs x 66.5 KB, 68 MB on a 256-CU MI355X).  The tables
+ * work-groups: 2 x CUs x 130 KB, 68 MB on a 256-CU MI355X).  The tables
  * are immutable after creation; rf_rope3d_apply and rf_kvcache_roll may use
  * one context from several threads and streams.  rf_window_attention calls
  * that share a context share its workspace and must be ordered (one stream,
@@ -203,17 +203,19 @@ typedef struct {
  * attention kernel (vibeleaderboard digest, key takeaways).
  *
  * For each segment, head h and query token i:
- *   q^ = bf16 RoPE of q_i at its position (as rf_rope3d_apply),
- *   s_j = scale * <q^, k_j>  over every token j of the context frames
- *         (k_j as stored: already rotated),
+ *   s_j = scale * <RoPE(q_i), k_j>  over every token j of the context frames
+ *         (RoPE at the query's position, as rf_rope3d_apply; k_j as stored:
+ *         already rotated),
  *   o_i = sum_j softmax(s)_j v_j, written as bf16 (round to nearest even).
- * Scores, the softmax and the accumulators are float32; the softmax weights
- * enter the value product as bf16.  scale == 0 means 1/sqrt(head_dim).
+ * Precision: the rotated query, times scale*log2(e), is rounded to bf16 once
+ * (the same relative error as rounding the rotated query itself); scores,
+ * the softmax and the accumulators are float32; the softmax weights enter
+ * the value product as bf16.  scale == 0 means 1/sqrt(head_dim).
  * The context length is a runtime argument (whole frames); nothing is
  * recompiled or reallocated when it changes.
  *
- * Work split: query tiles of 128 rows run whole on the GPU's work-group
- * slots in full rounds; the tiles of a last, partly filled round are cut
+ * Work split: query tiles of 256 rows run whole on the GPU's work-group
+ * slots (one per CU) in full rounds; the tiles of a last, partly filled round are cut
  * along their keys into equal shares for all slots and merged by a second
  * kernel on the same stream (the result does not depend on the split beyond
  * float32 rounding; it is deterministic for a given launch shape).

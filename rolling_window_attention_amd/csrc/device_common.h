@@ -78,6 +78,26 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, int p0, int64_t t, int r, i
   return y;
 }
 
+// As rope_chunk, with the rotated pair scaled by `scale` in float64 before its
+// single rounding to bf16 (the attention kernel's pre-scaled query operand).
+__device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, int p0, int64_t t, int r, int c,
+                                                   const RopeTables& T, double scale) {
+  uint32_t in[4] = {x[0], x[1], x[2], x[3]};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float2 cs = rope_cs(T, p0 + k, t, r, c);
+    double x0 = (double)bf16_to_f32(in[k] & 0xFFFFu);
+    double x1 = (double)bf16_to_f32(in[k] >> 16);
+    double cc = (double)cs.x, ss = (double)cs.y;
+    double y0 = (x0 * cc - x1 * ss) * scale;
+    double y1 = (x0 * ss + x1 * cc) * scale;
+    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+  }
+  u32x4 y = {out[0], out[1], out[2], out[3]};
+  return y;
+}
+
 // Exact unsigned division n / d for n < 2^24, d >= 1: a float estimate is off
 // by at most one and is corrected with one multiply-subtract.
 __device__ __forceinline__ uint32_t small_div(uint32_t n, uint32_t d, float inv_d, uint32_t* rem) {

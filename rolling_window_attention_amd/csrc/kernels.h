@@ -10,9 +10,9 @@ namespace rfattn {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxSegments = 8;
-constexpr int kAttnBlockM = 128;   // query rows per attention work item
+constexpr int kAttnBlockM = 256;   // query rows per attention work item
 constexpr int kAttnBlockN = 64;    // keys per key tile (one work unit per key tile)
-constexpr int kWorkersPerCu = 2;   // persistent attention work-groups per CU
+constexpr int kWorkersPerCu = 1;   // persistent attention work-groups per CU
 // One partial result of a split query tile: O [rows][head_dim], m [rows], l [rows].
 constexpr int kPartRows = kAttnBlockM;
 constexpr int kPartFloats = kPartRows * kHeadDim + 2 * kPartRows;

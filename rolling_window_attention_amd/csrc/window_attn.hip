@@ -8,8 +8,8 @@
 // passes are batched ("Optimizing Real-Time Video Generation on Trainium
 // Chips", section 8) -- here as several query segments in one launch.
 //
-// Work split.  A launch's query tiles -- (segment, head, 128 query rows) --
-// fill whole rounds of the GPU's work-group slots (two per CU) in the
+// Work split.  A launch's query tiles -- (segment, head, 256 query rows) --
+// fill whole rounds of the GPU's work-group slots (one per CU) in the
 // ordinary way: one work-group per tile, numbered so that each XCD walks
 // consecutive tiles of one head and its resident work-groups read the same
 // K/V tiles at about the same time (L2 reuse).  The tiles left over for a
@@ -21,10 +21,16 @@
 // window_attn_fixup merges the pieces.  A launch with fewer tiles than slots
 // (the cache-update pass alone) is split this way entirely.
 //
-// Per query tile: four waves of 32 query rows.  Per 64-key tile:
-//   S^T[key][q] = K_tile . Q^T      v_mfma_f32_32x32x16_bf16, 2 key blocks x 8 k-steps
-//   online softmax in float32, exp2 with scale*log2(e) folded into one FMA
-//   O^T[d][q]  += V^T_tile . P^T    4 dim blocks x 4 k-steps
+// Per query tile: eight waves of 32 query rows (two per SIMD) share each K/V
+// tile, which the work-group fetches and stages once.  Per 64-key tile:
+//   T^T[key][q] = K_tile . Q'^T - m  v_mfma_f32_32x32x16_bf16, 2 key blocks x (8+1) k-steps
+//   online softmax in float32: 2^T, bf16 weights P, row sums
+//   O^T[d][q]  += V^T_tile . P^T     4 dim blocks x 4 k-steps
+// Q' is Q rotated (3D-RoPE) and scaled by scale*log2(e) on load, so the score
+// MFMAs deliver exponents in log2 units; the ninth k-step of each key block
+// subtracts the running row max m (A: 1 in k-slot 0 for every key, B: -m in
+// k-slot 0 for every query).  The softmax is then one exp2, half a pack and
+// half a dot2 per score, plus the tile max.
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so a row max needs one cross-half exchange, the row sum
 // none until the end, and the rescale is a per-lane scalar.  The key order
@@ -32,14 +38,16 @@
 // values per key block are 16 consecutive keys, which is what the P^T
 // operand of the value product needs; the softmax is order-free over keys.
 //
-// Software pipeline per wave, iteration j: the score MFMAs of tile j are
-// issued next to the softmax of tile j-1, then the value MFMAs of tile j-1
-// next to staging the following K/V tiles.  K/V tiles are gathered from the
-// ring slots (a tile may straddle two frames) with raw buffer loads into
-// registers and written to padded LDS rows one iteration later; the K
-// pipeline runs one tile ahead of the V pipeline.  Q is loaded with 3D-RoPE
-// applied on the fly (bit-identical to rf_rope3d_apply); keys are stored
-// rotated in the ring.
+// Software pipeline per wave, step j: stage K_{j+1} and V_j (fetched one step
+// earlier into registers) to LDS and fetch K_{j+2} and V_{j+1} from the ring;
+// softmax and value MFMAs of tile j-1; score MFMAs of tile j into the same
+// registers; one barrier.  The two waves of a SIMD belong to different
+// phases most of the time, and the MFMA blocks run at raised priority, so
+// one wave's softmax fills the other's MFMA time.  K/V tiles are gathered
+// from the ring slots with raw buffer loads: a tile inside one frame takes a
+// fixed lane offset plus a scalar base; a tile straddling two frames (or past
+// the context's end) takes per-row offsets.  LDS rows are padded for
+// conflict-free 16-byte fragment reads.  Keys are stored rotated in the ring.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -53,7 +61,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockM = kAttnBlockM;       // query rows per work item (128)
 constexpr int kBlockN = kAttnBlockN;       // keys per tile (64)
-constexpr int kThreads = 256;              // 4 waves
+constexpr int kThreads = 512;              // 8 waves of 32 query rows
 constexpr int kKRow = kHeadDim + 8;        // LDS row stride of K tile (272 B: conflict-free 16 B reads)
 constexpr int kVRow = kBlockN + 8;         // LDS row stride of V^T tile (144 B)
 constexpr int kKTile = kBlockN * kKRow;    // elements
@@ -101,6 +109,13 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return rem * per + (x - rem) * (per - 1) + idx;
 }
 
+// Round x up to a bf16-representable float (towards +infinity).
+__device__ __forceinline__ float bf16_ceil(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (x > 0.0f) b += 0xFFFFu;
+  return __uint_as_float(b & 0xFFFF0000u);
+}
+
 // One work item: query tile qt of head h of segment sg, key tiles [ka, kb).
 // A complete item (all key tiles) writes the normalised bf16 output; a piece
 // of a split tile writes its partial result to `part`.
@@ -113,7 +128,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const int lr = lane & 31;  // query column of this lane in the 32x32 tiles
   const int hf = lane >> 5;  // lane half: selects k-slots 0-7 / 8-15 of an MFMA step
 
-  // ---- Q fragment, RoPE'd on load: lane holds query row lr, dims 16s+8hf..+7 --
+  // ---- Q fragment: RoPE'd and scaled by c = scale*log2(e) on load, rounded to
+  // bf16 once; lane holds query row lr, dims 16s+8hf..+7.  The score MFMAs then
+  // yield scaled scores in log2 units directly.
   const int qi = qt * kBlockM + wave * 32 + lr;
   const bool qvalid = qi < sg.q_tokens;
   bf16x8 qf[8];
@@ -123,11 +140,12 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     const int row = pin / a.gw;
     const int col = pin - row * a.gw;
     const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;
+    const double cl64 = (double)a.c_log2;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = 2 * s + hf;
       u32x4 x = *(const u32x4*)(qrow + 8 * c);
-      qf[s] = as_bf16x8(rope_chunk(x, 4 * c, sg.q_t0 + f, row, col, a.tab));
+      qf[s] = as_bf16x8(rope_chunk_scaled(x, 4 * c, sg.q_t0 + f, row, col, a.tab, cl64));
     }
   } else {
 #pragma unroll
@@ -150,10 +168,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_ring), 0, (int)ring_b, kBufferWord3);
   const uint32_t k_head = (uint32_t)h * (uint32_t)N * (kHeadDim * 2u);  // K: [H][N][D]
   const uint32_t v_head = (uint32_t)h * kHeadDim * (uint32_t)N * 2u;    // V: [H][D][N]
-  // K: rows (tid>>4) + 16i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 32i, key chunk tid&7.
+  // K: rows (tid>>4) + 32i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 64i, key chunk tid&7.
   const int k_r0 = tid >> 4, k_c = tid & 15;
   const int v_d0 = tid >> 3, v_kc = tid & 7;
-  u32x4 kst[4], vst[4];
+  // Lane parts of the byte offsets for a tile inside one frame; row i adds a
+  // uniform 32*i rows (K) or 64*i dims (V), carried in the scalar offset.
+  const uint32_t k_lane = (uint32_t)k_r0 * (kHeadDim * 2u) + 16u * k_c;
+  const uint32_t v_lane = (uint32_t)v_d0 * (uint32_t)N * 2u + 16u * v_kc;
+  u32x4 kst[2], vst[2];
 
   // Cursors of the next tile to load (uniform): slot and token offset of its
   // first key, starting at key tile ka.
@@ -176,29 +198,38 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
 
   auto load_k = [&]() {
     const int key_lim = nkeys - kload * kBlockN;  // valid keys in this tile (may be <= 0)
-    uint32_t off[4];
-    if constexpr (!kSmallN) {
-      const int b = N - kn;  // keys of this tile still in the current frame
-      const int nxt = (kslot + 1 == W) ? 0 : kslot + 1;
-      const uint32_t ka = (uint32_t)kslot * slot_b + k_head + (uint32_t)kn * (kHeadDim * 2u);
-      const uint32_t kb = (uint32_t)nxt * slot_b + k_head - (uint32_t)b * (kHeadDim * 2u);
+    if (!kSmallN && kn + kBlockN <= N && key_lim >= kBlockN) {
+      // whole tile in one frame, all keys valid: lane offset + uniform offset
+      const uint32_t base = (uint32_t)kslot * slot_b + k_head + (uint32_t)kn * (kHeadDim * 2u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = k_r0 + 16 * i;
-        off[i] = (uint32_t)r * (kHeadDim * 2u) + 16u * k_c + (r < b ? ka : kb);
-      }
+      for (int i = 0; i < 2; ++i)
+        kst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               krs, k_lane, base + (uint32_t)i * (32u * kHeadDim * 2u), 0));
     } else {
+      uint32_t off[2];
+      if constexpr (!kSmallN) {
+        const int b = N - kn;  // keys of this tile still in the current frame
+        const int nxt = (kslot + 1 == W) ? 0 : kslot + 1;
+        const uint32_t ba = (uint32_t)kslot * slot_b + k_head + (uint32_t)kn * (kHeadDim * 2u);
+        const uint32_t bb = (uint32_t)nxt * slot_b + k_head - (uint32_t)b * (kHeadDim * 2u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int n = kn + k_r0 + 16 * i, slot = kslot;
-        while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
-        off[i] = (uint32_t)slot * slot_b + k_head + (uint32_t)n * (kHeadDim * 2u) + 16u * k_c;
+        for (int i = 0; i < 2; ++i) {
+          const int r = k_r0 + 32 * i;
+          off[i] = (uint32_t)r * (kHeadDim * 2u) + 16u * k_c + (r < b ? ba : bb);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          int n = kn + k_r0 + 32 * i, slot = kslot;
+          while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
+          off[i] = (uint32_t)slot * slot_b + k_head + (uint32_t)n * (kHeadDim * 2u) + 16u * k_c;
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (k_r0 + 16 * i >= key_lim) off[i] = kOutOfRange;  // past the end: zeros
-      kst[i] = bload(krs, off[i]);
+      for (int i = 0; i < 2; ++i) {
+        if (k_r0 + 32 * i >= key_lim) off[i] = kOutOfRange;  // past the end: zeros
+        kst[i] = bload(krs, off[i]);
+      }
     }
     advance(kslot, kn);
     ++kload;
@@ -206,22 +237,30 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
 
   auto load_v = [&]() {
     const int key_lim = nkeys - vload * kBlockN;
-    uint32_t base;
-    if constexpr (!kSmallN) {
-      const int b = N - vn;
-      const int nxt = (vslot + 1 == W) ? 0 : vslot + 1;
-      base = (8 * v_kc < b) ? (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u
-                            : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
-    } else {
-      int n = vn + 8 * v_kc, slot = vslot;
-      while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
-      base = (uint32_t)slot * slot_b + v_head + (uint32_t)n * 2u - 16u * v_kc;
-    }
-    const bool valid = 8 * v_kc < key_lim;
+    if (!kSmallN && vn + kBlockN <= N && key_lim >= kBlockN) {
+      const uint32_t base = (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = base + (uint32_t)(v_d0 + 32 * i) * (uint32_t)N * 2u + 16u * v_kc;
-      vst[i] = bload(vrs, valid ? off : kOutOfRange);
+      for (int i = 0; i < 2; ++i)
+        vst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               vrs, v_lane, base + (uint32_t)i * 128u * (uint32_t)N, 0));
+    } else {
+      uint32_t base;
+      if constexpr (!kSmallN) {
+        const int b = N - vn;
+        const int nxt = (vslot + 1 == W) ? 0 : vslot + 1;
+        base = (8 * v_kc < b) ? (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u
+                              : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
+      } else {
+        int n = vn + 8 * v_kc, slot = vslot;
+        while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
+        base = (uint32_t)slot * slot_b + v_head + (uint32_t)n * 2u - 16u * v_kc;
+      }
+      const bool valid = 8 * v_kc < key_lim;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t off = base + (uint32_t)(v_d0 + 64 * i) * (uint32_t)N * 2u + 16u * v_kc;
+        vst[i] = bload(vrs, valid ? off : kOutOfRange);
+      }
     }
     advance(vslot, vn);
     ++vload;
@@ -230,12 +269,12 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   auto store_k = [&](int buf) {
     uint16_t* Kl = lds + buf * kKTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(Kl + (k_r0 + 16 * i) * kKRow + 8 * k_c) = kst[i];
+    for (int i = 0; i < 2; ++i) *(u32x4*)(Kl + (k_r0 + 32 * i) * kKRow + 8 * k_c) = kst[i];
   };
   auto store_v = [&](int buf) {
     uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(Vl + (v_d0 + 32 * i) * kVRow + 8 * v_kc) = vst[i];
+    for (int i = 0; i < 2; ++i) *(u32x4*)(Vl + (v_d0 + 64 * i) * kVRow + 8 * v_kc) = vst[i];
   };
 
   // ---- running state -----------------------------------------------------------
@@ -244,9 +283,13 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-  float m_run = -1.0e30f;  // running row max of scaled scores (log2 units), maybe stale by < 8
-  float l_run = 0.0f;      // this lane's partial row sum of the bf16 weights
-  const float cl = a.c_log2;
+  // Running row max m (log2 units), kept bf16-representable: the score MFMAs
+  // subtract it themselves through one more k-step whose A operand is 1 in
+  // k-slot 0 (all keys) and whose B operand is -m in k-slot 0 (per query).
+  float m_run = 0.0f;
+  float l_run = 0.0f;  // this lane's partial row sum of the bf16 weights
+  const u32x4 ones_a = {hf == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
+  u32x4 negm_b = {0u, 0u, 0u, 0u};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16 zero16 = {};
 
@@ -254,14 +297,15 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   // output register i then holds key 16*hf + i of each 32-key block.
   const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
 
-  // S^T = K Q^T for keys [0,32) and [32,64) of the tile in K buffer `buf`
+  // T^T = K Q'^T - m for keys [0,32) and [32,64) of the tile in K buffer `buf`
+  // (Q' = c Q): the exponents of the softmax weights in log2 units.
   // Both MFMA blocks run at raised wave priority: while one wave of a SIMD
   // issues its MFMAs, the other wave's softmax VALU work fills the gaps.
   auto scores = [&](int buf, f32x16& s0, f32x16& s1) {
     const uint16_t* Kl = lds + buf * kKTile;
     __builtin_amdgcn_s_setprio(1);
-    s0 = zero16;
-    s1 = zero16;
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 k0 = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
@@ -272,10 +316,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Online softmax of one tile's scores (log2 domain) into bf16 weights pw.
-  // The running max only moves when some row's tile max exceeds it by more
-  // than 2^8 (wave-uniform decision); then alpha rescales l here and O later.
-  auto softmax = [&](f32x16& s0, f32x16& s1, u32x4 (&pw)[4], bool& rescale, float& alpha) {
+  // Row max of a tile's exponents (both lane halves).
+  auto tile_max = [&](const f32x16& s0, const f32x16& s1) -> float {
     float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
 #pragma unroll
     for (int i = 2; i < 16; i += 2)
@@ -283,19 +325,41 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
 #pragma unroll
     for (int i = 0; i < 16; i += 2)
       mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
-    const float mt = xhalf_max(mx) * cl;
-    rescale = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
-    const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    return xhalf_max(mx);
+  };
+
+  // Move the running max up by delta (bf16-representable m_new - m_run > 0):
+  // shift this tile's exponents, rescale l and O, refresh -m for the MFMAs.
+  auto raise_max = [&](float m_new, f32x16& s0, f32x16& s1) {
+    const float delta = m_new - m_run;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] -= delta;
+      s1[i] -= delta;
+    }
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
     l_run *= alpha;
-    const float neg_m = -m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    m_run = m_new;
+    negm_b[0] = hf == 0 ? (__float_as_uint(-m_new) >> 16) : 0u;
+  };
+
+  // Online softmax of one tile: the running max only moves when some row's
+  // exponent exceeds 8 (wave-uniform decision, weights stay <= 2^8 meanwhile);
+  // then bf16 weights 2^t into pw, summed into l.
+  auto softmax = [&](f32x16& s0, f32x16& s1, u32x4 (&pw)[4]) {
+    const float mt = tile_max(s0, s1);
+    if (__builtin_amdgcn_ballot_w64(mt > kRescaleLog2) != 0)
+      raise_max(bf16_ceil(m_run + fmaxf(mt, 0.0f)), s0, s1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e], cl, neg_m));
-      const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], cl, neg_m));
-      const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e], cl, neg_m));
-      const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], cl, neg_m));
+      const float a0 = __builtin_amdgcn_exp2f(s0[2 * e]);
+      const float a1 = __builtin_amdgcn_exp2f(s0[2 * e + 1]);
+      const float b0 = __builtin_amdgcn_exp2f(s1[2 * e]);
+      const float b1 = __builtin_amdgcn_exp2f(s1[2 * e + 1]);
       const uint32_t pa = pack2(a0, a1), pb = pack2(b0, b1);
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa), ones, l_run, false);
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
@@ -323,65 +387,64 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     __builtin_amdgcn_s_setprio(0);
   };
 
-  auto rescale_o = [&](bool rescale, float alpha) {
-    if (rescale) {
+  // Keys past the end of the context (only in key tile key_tiles-1) get no weight.
+  auto mask_tail = [&](int tile, f32x16& s0, f32x16& s1) {
+    const int key_lim = nkeys - tile * kBlockN;
+    if (key_lim < kBlockN) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        if (16 * hf + i >= key_lim) s0[i] = -INFINITY;
+        if (32 + 16 * hf + i >= key_lim) s1[i] = -INFINITY;
+      }
     }
   };
 
   // ---- software pipeline over key tiles ----------------------------------------
-  // iteration j: scores of tile j | softmax of tile j-1 ; values of tile j-1 |
-  // stage K_{j+1} and V_j to LDS ; fetch K_{j+2} and V_{j+1} from the ring.
+  // step j: softmax and values of tile j-1, then the scores of tile j into the
+  // same registers; stage K_{j+1} and V_j to LDS; fetch K_{j+2} and V_{j+1}.
   load_k();  // K_0
   load_v();  // V_0
   store_k(0);
   store_v(0);
   load_k();  // K_1
   __syncthreads();
-  f32x16 sp0, sp1;  // scores of the previous tile
-  scores(0, sp0, sp1);
+  f32x16 x0, x1;
+  scores(0, x0, x1);  // m = 0: the plain scaled scores
+  if (ntiles == 1) mask_tail(kb - 1, x0, x1);
+  {  // first tile: the running max starts at its (rounded up) row max
+    const float m0 = bf16_ceil(tile_max(x0, x1));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x0[i] -= m0;
+      x1[i] -= m0;
+    }
+    m_run = m0;
+    negm_b[0] = hf == 0 ? (__float_as_uint(-m0) >> 16) : 0u;
+  }
   store_k(1);
   load_k();  // K_2
   load_v();  // V_1
   __syncthreads();
 
-  for (int j = 1; j < ntiles; ++j) {
-    f32x16 sn0, sn1;
+  auto step = [&](int j, f32x16& p0, f32x16& p1) {
     u32x4 pw[4];
-    bool rs;
-    float alpha;
-    scores(j & 1, sn0, sn1);
-    softmax(sp0, sp1, pw, rs, alpha);
-    rescale_o(rs, alpha);
-    values((j - 1) & 1, pw);
     store_k((j + 1) & 1);  // K_{j+1}
     store_v(j & 1);        // V_j
     load_k();              // K_{j+2}
     load_v();              // V_{j+1}
+    softmax(p0, p1, pw);
+    values((j - 1) & 1, pw);
+    scores(j & 1, p0, p1);
     __syncthreads();
-    sp0 = sn0;
-    sp1 = sn1;
-  }
-
-  {  // last tile: mask keys past the end, then its softmax and values
-    const int key_lim = nkeys - (kb - 1) * kBlockN;
-    if (key_lim < kBlockN) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (16 * hf + i >= key_lim) sp0[i] = -INFINITY;
-        if (32 + 16 * hf + i >= key_lim) sp1[i] = -INFINITY;
-      }
-    }
+  };
+  auto finish = [&](f32x16& p0, f32x16& p1) {  // last tile: mask, softmax, values
+    mask_tail(kb - 1, p0, p1);
     u32x4 pw[4];
-    bool rs;
-    float alpha;
-    softmax(sp0, sp1, pw, rs, alpha);
-    rescale_o(rs, alpha);
+    softmax(p0, p1, pw);
     values((ntiles - 1) & 1, pw);
-  }
+  };
+  for (int j = 1; j < ntiles; ++j) step(j, x0, x1);
+  finish(x0, x1);
 
   // ---- epilogue --------------------------------------------------------------------
   const float l_tot = xhalf_sum(l_run);
@@ -436,7 +499,7 @@ __device__ __forceinline__ int unit_segment(const AttnArgs& a, uint32_t u) {
 // general per-row frame walk is used.  Otherwise a tile straddles at most one
 // frame boundary and each row picks one of two bases.
 template <bool kSmallN>
-__global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   if ((int)blockIdx.x < a.dp_tiles) {
     // whole query tiles, one per work-group, in XCD-contiguous order
@@ -478,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void window_attn_kernel(AttnArgs a) {
 // range and continue past it: worker v holds the first piece (in its slot 0
 // if the tile starts its range, else slot 1), the following workers the
 // next pieces (their slot 0).  O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i.
-__global__ __launch_bounds__(256) void window_attn_fixup(AttnArgs a) {
+__global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
   const uint32_t P = (uint32_t)a.n_workers;
   const uint32_t span = a.total_units - a.sk_unit_begin;
   const uint32_t v = blockIdx.x;
@@ -547,7 +610,7 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(window_attn_kernel<false>, grid, dim3(kThreads), kLdsBytes, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_workers == 0) return e;
-  hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.n_workers), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.n_workers), dim3(2 * kPartRows), 0, s, a);
   return hipGetLastError();
 }
 
