@@ -38,16 +38,17 @@
 // values per key block are 16 consecutive keys, which is what the P^T
 // operand of the value product needs; the softmax is order-free over keys.
 //
-// Software pipeline per wave, step j: stage K_{j+1} and V_j (fetched one step
-// earlier into registers) to LDS and fetch K_{j+2} and V_{j+1} from the ring;
-// softmax and value MFMAs of tile j-1; score MFMAs of tile j into the same
-// registers; one barrier.  The two waves of a SIMD belong to different
-// phases most of the time, and the MFMA blocks run at raised priority, so
-// one wave's softmax fills the other's MFMA time.  K/V tiles are gathered
-// from the ring slots with raw buffer loads: a tile inside one frame takes a
-// fixed lane offset plus a scalar base; a tile straddling two frames (or past
-// the context's end) takes per-row offsets.  LDS rows are padded for
-// conflict-free 16-byte fragment reads.  Keys are stored rotated in the ring.
+// Schedule: the eight waves form two groups (waves 0-3 and 4-7, one wave of
+// each per SIMD) that play ping-pong.  A key-tile step has two halves
+// separated by work-group barriers: an MFMA half (value MFMAs of tile j-1,
+// score MFMAs of tile j) and a softmax half (weights of tile j; staging of
+// the group's share of the next K/V tiles).  Group 1 runs one half behind
+// group 0, so on every SIMD one wave issues MFMAs while the other does its
+// softmax.  K/V tiles are gathered from the ring slots with raw buffer loads
+// into registers and written to padded LDS rows (conflict-free 16-byte
+// fragment reads) one step later: a tile inside one frame takes a fixed lane
+// offset plus a scalar base; a tile straddling two frames (or past the
+// context's end) takes per-row offsets.  Keys are stored rotated in the ring.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -298,20 +299,27 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
 
   // T^T = K Q'^T - m for keys [0,32) and [32,64) of the tile in K buffer `buf`
-  // (Q' = c Q): the exponents of the softmax weights in log2 units.
-  // Both MFMA blocks run at raised wave priority: while one wave of a SIMD
-  // issues its MFMAs, the other wave's softmax VALU work fills the gaps.
+  // (Q' = c Q): the exponents of the softmax weights in log2 units.  All 16
+  // K fragments are read before the first MFMA (sched_barrier keeps the
+  // compiler from sinking the reads next to their MFMAs), so LDS latency is
+  // paid once per block.
+  // Both MFMA blocks run at raised wave priority.
   auto scores = [&](int buf, f32x16& s0, f32x16& s1) {
     const uint16_t* Kl = lds + buf * kKTile;
     __builtin_amdgcn_s_setprio(1);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
+    bf16x8 kf[16];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 k0 = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
-      const bf16x8 k1 = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+      kf[2 * s] = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
+      kf[2 * s + 1] = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * s], qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * s + 1], qf[s], s1, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -368,22 +376,22 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     }
   };
 
-  // O^T += V^T P^T with the values in V buffer `buf`
+  // O^T += V^T P^T with the values in V buffer `buf` (fragments read up front)
   auto values = [&](int buf, const u32x4 (&pw)[4]) {
     const uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
     __builtin_amdgcn_s_setprio(1);
+    bf16x8 vf[16];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int bu = 0; bu < 4; ++bu)
+        vf[4 * dt + bu] = *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * (bu >> 1) + 16 * hf + 8 * (bu & 1));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 vf =
-              *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * b + 16 * hf + 8 * u);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw[2 * b + u]), o[dt], 0, 0, 0);
-        }
-      }
-    }
+    for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * dt + bu], as_bf16x8(pw[bu]), o[dt], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -399,52 +407,54 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     }
   };
 
-  // ---- software pipeline over key tiles ----------------------------------------
-  // step j: softmax and values of tile j-1, then the scores of tile j into the
-  // same registers; stage K_{j+1} and V_j to LDS; fetch K_{j+2} and V_{j+1}.
+  // ---- software pipeline over key tiles: two wave groups in ping-pong --------
+  // Group 0 (waves 0-3) and group 1 (waves 4-7) put one wave on each SIMD.
+  // Each step has two halves separated by barriers: an MFMA half (values of
+  // tile j-1, scores of tile j) and a softmax half (weights of tile j, and
+  // staging this group's share of the next K/V tiles).  Group 1 runs one half
+  // behind group 0, so on every SIMD one wave's MFMAs overlap the other
+  // wave's softmax.  Group g stages K_{j+1+g} and V_{j+g} in the softmax half
+  // of step j: both shares of K_{j+1}, V_j are in LDS before group 0's MFMA
+  // half of step j+1, and no buffer is written while a group still reads it.
+  const int grp = __builtin_amdgcn_readfirstlane(wave) >> 2;  // wave-uniform
   load_k();  // K_0
-  load_v();  // V_0
   store_k(0);
-  store_v(0);
   load_k();  // K_1
+  load_v();  // V_0
   __syncthreads();
-  f32x16 x0, x1;
-  scores(0, x0, x1);  // m = 0: the plain scaled scores
-  if (ntiles == 1) mask_tail(kb - 1, x0, x1);
-  {  // first tile: the running max starts at its (rounded up) row max
-    const float m0 = bf16_ceil(tile_max(x0, x1));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      x0[i] -= m0;
-      x1[i] -= m0;
-    }
-    m_run = m0;
-    negm_b[0] = hf == 0 ? (__float_as_uint(-m0) >> 16) : 0u;
-  }
-  store_k(1);
-  load_k();  // K_2
-  load_v();  // V_1
-  __syncthreads();
-
-  auto step = [&](int j, f32x16& p0, f32x16& p1) {
-    u32x4 pw[4];
-    store_k((j + 1) & 1);  // K_{j+1}
-    store_v(j & 1);        // V_j
-    load_k();              // K_{j+2}
-    load_v();              // V_{j+1}
-    softmax(p0, p1, pw);
-    values((j - 1) & 1, pw);
-    scores(j & 1, p0, p1);
+  if (grp == 1) {  // group 1's extra first half
+    store_k(1);
+    store_v(0);
+    load_k();  // K_2
+    load_v();  // V_1
     __syncthreads();
-  };
-  auto finish = [&](f32x16& p0, f32x16& p1) {  // last tile: mask, softmax, values
-    mask_tail(kb - 1, p0, p1);
-    u32x4 pw[4];
-    softmax(p0, p1, pw);
-    values((ntiles - 1) & 1, pw);
-  };
-  for (int j = 1; j < ntiles; ++j) step(j, x0, x1);
-  finish(x0, x1);
+  }
+  f32x16 x0, x1;
+  u32x4 pw[4];
+  for (int j = 0; j < ntiles; ++j) {
+    if (j > 0) values((j - 1) & 1, pw);
+    scores(j & 1, x0, x1);
+    __syncthreads();
+    if (j == ntiles - 1) mask_tail(kb - 1, x0, x1);
+    if (j == 0) {  // first tile: the running max starts at its (rounded up) row max
+      const float m0 = bf16_ceil(tile_max(x0, x1));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x0[i] -= m0;
+        x1[i] -= m0;
+      }
+      m_run = m0;
+      negm_b[0] = hf == 0 ? (__float_as_uint(-m0) >> 16) : 0u;
+    }
+    softmax(x0, x1, pw);
+    store_k((j + 1 + grp) & 1);
+    store_v((j + grp) & 1);
+    load_k();
+    load_v();
+    __syncthreads();
+  }
+  values((ntiles - 1) & 1, pw);
+  if (grp == 0) __syncthreads();  // the same barrier count as group 1
 
   // ---- epilogue --------------------------------------------------------------------
   const float l_tot = xhalf_sum(l_run);
