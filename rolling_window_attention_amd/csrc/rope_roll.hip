@@ -14,50 +14,72 @@
 
 namespace rfattn {
 
-// ---------------------------------------------------------------------------
-// rope3d: each work-group owns kRopeTok consecutive tokens; each thread takes
-// up to kRopeBatch of their 16-byte chunks (stride: the block size), issues
-// all loads before any store, then rotates and stores -- so a thread keeps
-// kRopeBatch loads in flight instead of waiting for each (in-place use makes
-// the compiler keep every store behind the load of its own chunk only).
-// ---------------------------------------------------------------------------
-constexpr int kRopeTok = 8;
-constexpr int kRopeBatch = 8;
+// rope3d works on 16-byte chunks (8 bf16, 4 rotation pairs) spread over the
+// threads of a work-group: on gfx950 a streaming kernel reaches copy
+// bandwidth with one or two loads per thread in flight and many waves, and
+// loses it (down to ~60%) when a thread batches eight loads before its
+// stores.
 
-__global__ __launch_bounds__(256) void rope3d_kernel(RopeArgs a) {
-  const uint32_t row_chunks = (uint32_t)a.H * 16u;  // 16-byte chunks per token row
-  const uint32_t total = (uint32_t)kRopeTok * row_chunks;
-  const int64_t tok0 = (int64_t)blockIdx.x * kRopeTok;
+// Position of chunk q of a token-major [tokens][H*16 chunks] range: the
+// work-group's first token is found once (uniform division), the thread's
+// token by a small exact division of its offset from there.
+struct ChunkPos {
+  uint32_t tok;   // token index in the range
+  uint32_t hc;    // head * 16 + chunk
+};
+__device__ __forceinline__ ChunkPos chunk_pos(uint32_t blk_base, uint32_t row_chunks, float inv_row) {
+  const uint32_t tok0 = __builtin_amdgcn_readfirstlane(blk_base / row_chunks);
+  const uint32_t rem0 = blk_base - tok0 * row_chunks;
+  uint32_t hc;
+  const uint32_t tl = small_div(rem0 + threadIdx.x, row_chunks, inv_row, &hc);
+  return {tok0 + tl, hc};
+}
+
+// (frame offset, row, column) of token `tok` of a range whose token 0 starts
+// frame 0; frames have N tokens of gw columns.
+struct TokPos {
+  uint32_t f, row, col;
+};
+__device__ __forceinline__ TokPos tok_pos(uint32_t tok, uint32_t N, float inv_n, uint32_t gw, float inv_gw) {
+  uint32_t pin, col;
+  const uint32_t f = small_div(tok, N, inv_n, &pin);
+  const uint32_t row = small_div(pin, gw, inv_gw, &col);
+  return {f, row, col};
+}
+
+// ---------------------------------------------------------------------------
+// rope3d: thread = one chunk of the [n_tokens][H*16] range.
+// ---------------------------------------------------------------------------
+constexpr int kRopeThreads = 256;
+
+// Tokens [tok_base, tok_base + n) of the range, n * H * 16 < 2^31.  A
+// work-group covers kRopeU * 256 consecutive chunks; thread t takes chunks
+// t, t + 256, ...: all its loads are issued first, so each wave keeps kRopeU
+// loads in flight while it does the float64 rotation of the earlier ones.
+constexpr int kRopeU = 2;
+__global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a, uint32_t tok_base, uint32_t n) {
+  const uint32_t row_chunks = (uint32_t)a.H * 16u;
   const float inv_row = 1.0f / (float)row_chunks;
-  const float inv_n = 1.0f / (float)a.N;
-  const float inv_gw = 1.0f / (float)a.gw;
-  for (uint32_t q0 = threadIdx.x; q0 < total; q0 += kRopeBatch * blockDim.x) {
-    u32x4 v[kRopeBatch];
-    int64_t tok[kRopeBatch];
-    uint32_t hc[kRopeBatch];
-    bool ok[kRopeBatch];
+  u32x4 x[kRopeU];
+  ChunkPos cp[kRopeU];
 #pragma unroll
-    for (int i = 0; i < kRopeBatch; ++i) {
-      const uint32_t q = q0 + (uint32_t)i * blockDim.x;
-      uint32_t rem;
-      const uint32_t tl = small_div(q, row_chunks, inv_row, &rem);
-      tok[i] = tok0 + tl;
-      hc[i] = rem;  // head * 16 + chunk
-      ok[i] = q < total && tok[i] < a.n_tokens;
-      if (ok[i])
-        v[i] = __builtin_nontemporal_load((const u32x4*)(a.x + tok[i] * a.x_ld + (rem >> 4) * 128u + (rem & 15u) * 8u));
+  for (int u = 0; u < kRopeU; ++u) {
+    const uint32_t base = (blockIdx.x * (uint32_t)kRopeU + u) * (uint32_t)kRopeThreads;
+    cp[u] = chunk_pos(base, row_chunks, inv_row);
+    if (cp[u].tok < n) {
+      const uint32_t tok = tok_base + cp[u].tok;
+      x[u] = __builtin_nontemporal_load(
+          (const u32x4*)(a.x + (int64_t)tok * a.x_ld + (int64_t)(cp[u].hc >> 4) * 128 + (cp[u].hc & 15u) * 8));
     }
+  }
 #pragma unroll
-    for (int i = 0; i < kRopeBatch; ++i) {
-      if (!ok[i]) continue;
-      uint32_t pin;
-      const uint32_t f = small_div((uint32_t)tok[i], (uint32_t)a.N, inv_n, &pin);
-      uint32_t col;
-      const uint32_t row = small_div(pin, (uint32_t)a.gw, inv_gw, &col);
-      const uint32_t c = hc[i] & 15u;
-      const u32x4 y = rope_chunk(v[i], (int)c * 4, a.t0 + f, (int)row, (int)col, a.tab);
-      __builtin_nontemporal_store(y, (u32x4*)(a.y + tok[i] * a.y_ld + (hc[i] >> 4) * 128u + c * 8u));
-    }
+  for (int u = 0; u < kRopeU; ++u) {
+    if (cp[u].tok >= n) continue;
+    const uint32_t tok = tok_base + cp[u].tok;
+    const uint32_t c = cp[u].hc & 15u;
+    const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
+    const u32x4 y = rope_chunk(x[u], (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col, a.tab);
+    __builtin_nontemporal_store(y, (u32x4*)(a.y + (int64_t)tok * a.y_ld + (int64_t)(cp[u].hc >> 4) * 128 + c * 8));
   }
 }
 
@@ -139,10 +161,20 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a) {
   }
 }
 
+// Tokens per launch so that a launch's chunk indices stay below 2^31.
+static uint32_t tokens_per_launch(int H) { return (uint32_t)(((uint32_t)1 << 31) / ((uint32_t)H * 16u)) - 64u; }
+
 hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((a.n_tokens + kRopeTok - 1) / kRopeTok));
-  hipLaunchKernelGGL(rope3d_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  const uint32_t step = tokens_per_launch(a.H);
+  for (uint32_t t = 0; t < (uint32_t)a.n_tokens; t += step) {
+    const uint32_t n = min(step, (uint32_t)a.n_tokens - t);
+    const uint64_t chunks = (uint64_t)n * (uint64_t)a.H * 16u;
+    dim3 grid((unsigned)((chunks + kRopeThreads * kRopeU - 1) / (kRopeThreads * kRopeU)));
+    hipLaunchKernelGGL(rope3d_kernel, grid, dim3(kRopeThreads), 0, s, a, t, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
