@@ -113,52 +113,70 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   for (int i = 0; i < 8; ++i) { u32x4 r = {o[i][0], o[i][1], o[i][2], o[i][3]}; out[i] = r; }
 }
 
-__global__ __launch_bounds__(256) void roll_kernel(RollArgs a) {
-  const uint32_t L = blockIdx.x * 256u + threadIdx.x;
+// Work-groups [0, k_blocks): keys of tokens [tok_base, tok_base + k_tokens)
+// (k_tokens * H * 16 < 2^31), kRopeU chunks per thread as in rope3d, rotated
+// and stored to K[slot][h][n][d].  Work-groups from k_blocks on: value blocks,
+// a thread per 8 tokens x 8 dims of one (frame, head), transposed in registers
+// and stored to V[slot][h][d][n]; lane = 8*cc + gg (token group gg, dim chunk
+// cc), so every load and store instruction touches 8 runs of 128 bytes.
+__global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t k_blocks, uint32_t tok_base,
+                                                   uint32_t k_tokens) {
+  if (blockIdx.x < k_blocks) {
+    const uint32_t row_chunks = (uint32_t)a.H * 16u;
+    const float inv_row = 1.0f / (float)row_chunks;
+    u32x4 x[kRopeU];
+    ChunkPos cp[kRopeU];
+#pragma unroll
+    for (int u = 0; u < kRopeU; ++u) {
+      const uint32_t base = (blockIdx.x * (uint32_t)kRopeU + u) * 256u;
+      cp[u] = chunk_pos(base, row_chunks, inv_row);
+      if (cp[u].tok < k_tokens)
+        x[u] = __builtin_nontemporal_load((const u32x4*)(a.k_new + (int64_t)(tok_base + cp[u].tok) * a.k_ld +
+                                                         (int64_t)(cp[u].hc >> 4) * 128 + (cp[u].hc & 15u) * 8));
+    }
+#pragma unroll
+    for (int u = 0; u < kRopeU; ++u) {
+      if (cp[u].tok >= k_tokens) continue;
+      const uint32_t tok = tok_base + cp[u].tok;
+      const uint32_t h = cp[u].hc >> 4, c = cp[u].hc & 15u;
+      const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
+      int slot = a.slot0 + (int)p.f;
+      if (slot >= a.W) slot -= a.W;  // slot0 < W and f < W
+      const u32x4 y = rope_chunk(x[u], (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col, a.tab);
+      const uint32_t n = tok - p.f * (uint32_t)a.N;
+      __builtin_nontemporal_store(
+          y, (u32x4*)(a.k_ring + (int64_t)slot * a.slot_elems + ((int64_t)h * a.N + n) * 128 + c * 8));
+    }
+    return;
+  }
+  // value blocks: (frame, head) major, then 8-group blocks of 128 threads
+  const uint32_t groups = (uint32_t)a.N >> 3;
+  const uint32_t vb_per_fh = (((groups + 7) / 8) * 128 + 255) / 256;  // work-groups per (frame, head)
+  const uint32_t vb = blockIdx.x - k_blocks;
+  const uint32_t fh = vb / vb_per_fh;
+  const uint32_t L = (vb - fh * vb_per_fh) * 256u + threadIdx.x;
   const uint32_t gblock = L >> 7;           // 128 threads per 8 token groups x 16 chunks
   const uint32_t chalf = (L >> 6) & 1u;
   const uint32_t cc = (L >> 3) & 7u;
   const uint32_t gg = L & 7u;
   const uint32_t g = gblock * 8u + gg;      // token group (8 tokens)
   const uint32_t c = chalf * 8u + cc;       // dim chunk (8 dims)
-  const int fh = blockIdx.y;                // frame * H + head
-  const int f = fh / a.H;
-  const int h = fh - f * a.H;
-  const bool is_v = blockIdx.z != 0;        // z = 0: keys, z = 1: values
-  if (g >= (uint32_t)(a.N >> 3)) return;
-
+  const int f = (int)fh / a.H;
+  const int h = (int)fh - f * a.H;
+  if (g >= groups) return;
   int slot = a.slot0 + f;
-  if (slot >= a.W) slot -= a.W;  // slot0 < W and f < W
-  const int64_t t = a.t0 + f;
-
+  if (slot >= a.W) slot -= a.W;
   const uint32_t n0 = g * 8u;
   const int64_t in_tok0 = (int64_t)f * a.N + n0;
-  const uint16_t* src = is_v ? a.v_new : a.k_new;
-  const int64_t ld = is_v ? a.v_ld : a.k_ld;
   u32x4 in[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    in[j] = __builtin_nontemporal_load((const u32x4*)(src + (in_tok0 + j) * ld + h * 128 + c * 8));
-
-  if (!is_v) {
-    // Keys: rotate at (t, row, col) and store head-major.
-    uint32_t row = n0 / (uint32_t)a.gw;  // one division per thread; columns advance below
-    uint32_t col = n0 - row * (uint32_t)a.gw;
-    uint16_t* kslot = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)h * a.N * 128;
+    in[j] = __builtin_nontemporal_load((const u32x4*)(a.v_new + (in_tok0 + j) * a.v_ld + h * 128 + c * 8));
+  u32x4 vt[8];
+  transpose8x8(in, vt);
+  uint16_t* vslot = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * 128 * a.N;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 y = rope_chunk(in[j], (int)c * 4, t, (int)row, (int)col, a.tab);
-      *(u32x4*)(kslot + (int64_t)(n0 + j) * 128 + c * 8) = y;
-      if (++col == (uint32_t)a.gw) { col = 0; ++row; }
-    }
-  } else {
-    // Values: transpose the 8x8 block, store [d][n].
-    u32x4 vt[8];
-    transpose8x8(in, vt);
-    uint16_t* vslot = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * 128 * a.N;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4*)(vslot + (int64_t)(c * 8 + i) * a.N + n0) = vt[i];
-  }
+  for (int i = 0; i < 8; ++i) *(u32x4*)(vslot + (int64_t)(c * 8 + i) * a.N + n0) = vt[i];
 }
 
 // Tokens per launch so that a launch's chunk indices stay below 2^31.
@@ -178,11 +196,21 @@ hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
-  const unsigned groups = (unsigned)(a.N / 8);
-  const unsigned threads = ((groups + 7) / 8) * 128;  // 8-group blocks x 16 chunks
-  dim3 grid((threads + 255) / 256, (unsigned)(a.n_frames * a.H), 2);
-  hipLaunchKernelGGL(roll_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  const uint32_t tokens = (uint32_t)a.n_frames * (uint32_t)a.N;
+  const uint32_t step = tokens_per_launch(a.H);
+  const uint32_t groups = (uint32_t)a.N / 8u;
+  const uint32_t vb_per_fh = (((groups + 7) / 8) * 128 + 255) / 256;
+  const uint32_t v_blocks = (uint32_t)a.n_frames * (uint32_t)a.H * vb_per_fh;  // n_frames*H <= 65535
+  for (uint32_t t = 0; t < tokens; t += step) {
+    const uint32_t n = min(step, tokens - t);
+    const uint64_t k_chunks = (uint64_t)n * a.H * 16u;
+    const uint32_t k_blocks = (uint32_t)((k_chunks + 256u * kRopeU - 1) / (256u * kRopeU));
+    const uint32_t grid = k_blocks + (t == 0 ? v_blocks : 0u);  // value blocks ride with the first piece
+    hipLaunchKernelGGL(roll_kernel, dim3(grid), dim3(256), 0, s, a, k_blocks, t, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace rfattn
