@@ -157,12 +157,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t_start.elapsed_time(t_end) / args.steps
-    roll_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    roll_each = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_each = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    roll_ms = float(np.mean(roll_each))
+    attn_ms = float(np.mean(attn_each))
     last_s = step_idx[0] - 1
+
+    def pct(x):
+        return {f"p{q}": round(float(np.percentile(x, q)), 4) for q in (10, 50, 90)}
 
     # ---- extras (not part of the timed steps): denoise-only launch, standalone RoPE ----
     denoise_ms = rope_ms = None
+    cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
         p = pool[(last_s - s0) % args.pool]
@@ -182,6 +188,25 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         rope_ms = e0.elapsed_time(e1) / reps
+
+        # cold (a 1 GiB fill evicts L2 and the 256 MB MALL before each rep) and warm
+        # single-call times of the standalone RoPE and of the step's roll; the roll
+        # rewrites the last step's own frames, so the ring contents do not change
+        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+        p_last = pool[(last_s - s0) % args.pool]
+        single = {"rope3d_q": lambda: ctx.rope3d_apply(p["qa"], last_s, y=qr),
+                  "roll_16": lambda: cache.roll(p_last["k"], p_last["v"], last_s - 1)}
+        cold_warm = {}
+        for name, fn in single.items():
+            cold, warm = [], []
+            for _ in range(reps):
+                flush.zero_()
+                e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+                e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
+                warm.append(e0.elapsed_time(e1))
+            cold_warm[name] = (float(np.median(cold)), float(np.median(warm)))
+        del flush
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
@@ -226,6 +251,7 @@ def main():
         },
         "ms_attention": round(attn_ms, 4),
         "ms_roll": round(roll_ms, 4),
+        "per_launch_ms": {"attention": pct(attn_each), "roll": pct(roll_each)},
         "roll_GBps": round(roll_bytes / (roll_ms * 1e-3) / 1e9, 1),
         "roll_hbm_frac": round(roll_bytes / (roll_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "wall_s_timed": round(wall, 3),
@@ -240,6 +266,12 @@ def main():
             "tokens": 15 * N, "ms": round(rope_ms, 4),
             "GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes}
+        out["cold_warm"] = {
+            name: {"bytes": nbytes[name], "cold_ms": round(c, 4), "warm_ms": round(w, 4),
+                   "cold_hbm_frac": round(nbytes[name] / (c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "warm_hbm_frac": round(nbytes[name] / (w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for name, (c, w) in cold_warm.items()}
 
     if not args.no_cpu_baseline:
         ctx_frames = [written[t] for t in range(last_s - 6, last_s + 15)]
