@@ -92,13 +92,17 @@ def oracle_rows(geom, q_bits, q_t0, kh_frames, v_frames, rows, scale=None):
     return out
 
 
-def sample_rows(n_tokens, N, block_m=128, extra=64, seed=0):
-    """Rows that cover frame edges, tile edges, the ragged tail and random interior rows."""
+def sample_rows(n_tokens, N, block_m=256, extra=64, seed=0):
+    """Rows that cover frame edges, query-tile edges (block_m rows), the 32-row wave edges
+    of the first and the last (ragged) tile, and random interior rows."""
     rng = np.random.default_rng(seed)
     s = {0, 1, n_tokens - 1, n_tokens - 2}
     for f0 in range(0, n_tokens, N):
         s.update({f0, f0 + N - 1})
     last_tile = (n_tokens - 1) // block_m * block_m
-    s.update({last_tile, last_tile - 1, min(last_tile + 31, n_tokens - 1), min(last_tile + 32, n_tokens - 1)})
+    s.update({last_tile, last_tile - 1})
+    for base in (0, last_tile):
+        for w in range(0, block_m, 32):
+            s.update({base + w, base + w - 1, base + w + 31})
     s.update(int(x) for x in rng.integers(0, n_tokens, extra))
     return np.array(sorted(x for x in s if 0 <= x < n_tokens))

@@ -1,0 +1,118 @@
+"""GPU parity of rf_window_attention on inputs that stress the kernel's softmax and work
+split, against the float64 oracle (same tolerances as test_gpu_attention.py).
+
+* extreme softmax scales: 0.15 (logits with a standard deviation of ~2.5 in log2 units)
+  and 2^-10 (nearly uniform weights);
+* logits that start very negative and rise frame by frame (an offset of -20 log2 units at
+  the first context frame up to 0 at the last), so the running row max, negative at first,
+  rises by more than 8 several times as the kernel walks the context (the lazy rescale of
+  O and l with large shifts);
+* eight segments with different context ranges in one launch (the segment lookup of whole
+  tiles, of stream-K pieces and of the merge kernel).
+
+Every launch runs the batched layout (a 15-frame and a 1-frame segment over 21 frames,
+1,188 query tiles), so both whole tiles and key-split tiles are produced; rows are sampled
+at frame, tile, wave and tail boundaries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rolling_window_attention_amd as rf
+from rolling_window_attention_amd import synth
+
+from gpu_util import RotatedKeys, assert_close, down, f64, oracle_rows, sample_rows, up
+
+pytestmark = pytest.mark.gpu
+
+G = synth.FULL
+N = G.tokens_per_frame
+
+
+def _scaled(bits, alpha):
+    """bf16 bits times alpha, rounded back to bf16 (seeded test inputs)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(alpha)
+    return synth.f32_to_bf16_bits(f)
+
+
+# Dims 42 and 43 are the time axis's last rotation pair (22 pairs): its angle turns by
+# t * 10000^(-21/22) < 0.003 rad over 21 frames, so an offset there shifts every logit of
+# a frame by nearly the same amount whatever the query and key positions.
+def _offset(bits, delta, dims=(42, 43)):
+    f = (bits.astype(np.uint32) << 16).view(np.float32).copy()
+    f[..., list(dims)] += np.float32(delta)
+    return synth.f32_to_bf16_bits(f)
+
+
+def _ring(cfg, k_alpha=lambda t: 1.0, k_offset=lambda t: 0.0):
+    """A 21-frame ring holding frames 0..20; keys of frame t scaled by k_alpha(t), then
+    k_offset(t) added to dims 42 and 43 of every head (rounded back to bf16)."""
+    ctx = rf.Context(G.grid_h, G.grid_w, G.n_heads, G.head_dim, G.pairs, G.base, 4096)
+    cache = rf.KVCache(ctx, G.window)
+    data = {}
+    for t in range(G.window):
+        k = _scaled(synth.frame(G, cfg, 0, t, synth.K), k_alpha(t))
+        if k_offset(t) != 0.0:
+            k = _offset(k, k_offset(t))
+        data[t] = (k, synth.frame(G, cfg, 0, t, synth.V), ("stress", cfg))
+    cache.roll(up(np.concatenate([data[t][0] for t in range(G.window)])),
+               up(np.concatenate([data[t][1] for t in range(G.window)])), 0)
+    return ctx, cache, data
+
+
+def _check(data, q_bits, q_t0, o, ctx_lo, ctx_hi, rows, scale, what, rk):
+    khs = [rk.get(t, data[t][2], data[t][0]) for t in range(ctx_lo, ctx_hi)]
+    vs = [data[t][1] for t in range(ctx_lo, ctx_hi)]
+    want = oracle_rows(G, q_bits, q_t0, khs, vs, rows, scale=scale)
+    assert_close(f64(down(o))[rows], want, what)
+
+
+def _batched(cfg, scale=0.0, k_alpha=lambda t: 1.0, k_offset=lambda t: 0.0, q_offset=0.0, seed=0):
+    ctx, cache, data = _ring(cfg, k_alpha, k_offset)
+    qa = synth.frames(G, cfg, 0, 6, 15, synth.Q)
+    qb = synth.frame(G, cfg, 0, 5, synth.Q + synth.CLEAN)
+    if q_offset != 0.0:
+        qa, qb = _offset(qa, q_offset), _offset(qb, q_offset)
+    oa = torch.empty((15 * N, G.n_heads, G.head_dim), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty((N, G.n_heads, G.head_dim), dtype=torch.bfloat16, device="cuda")
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), 6, oa, 0, 21), rf.Segment(up(qb), 5, ob, 0, 21)],
+                        scale=scale)
+    torch.cuda.synchronize()
+    s = scale if scale > 0 else 1.0 / np.sqrt(G.head_dim)
+    rk = RotatedKeys(G)
+    _check(data, qa, 6, oa, 0, 21, sample_rows(15 * N, N, extra=40, seed=seed), s, f"{cfg} A", rk)
+    _check(data, qb, 5, ob, 0, 21, sample_rows(N, N, extra=24, seed=seed + 1), s, f"{cfg} B", rk)
+
+
+# Much larger logits amplify the bf16 rounding of the rotated inputs (which the float64
+# oracle does not have) to the size of the tolerance for any bf16 implementation: at
+# scale 0.25 a float64 emulation of bf16 operands alone already errs by 1.4e-2.
+@pytest.mark.parametrize("scale", [0.15, 2.0 ** -10])
+def test_extreme_scales(scale):
+    _batched(31 if scale > 0.1 else 32, scale=scale, seed=5)
+
+
+def test_running_max_rises_from_very_negative_logits():
+    # q offset 4 and key offset b = -20..0 on dims 42/43: logit offset 2*4*b/sqrt(128)
+    # = 0.71 b natural units = 1.02 b log2 units, from -20.4 up by 1.02 per frame
+    _batched(33, k_offset=lambda t: -20.0 + 1.0 * t, q_offset=4.0, seed=7)
+
+
+def test_eight_segments_one_launch():
+    """Segment i: query frame 7+i over context frames i..i+13 (14 frames); all eight in
+    one launch (672 query tiles over 256 work-group slots)."""
+    cfg = 35
+    ctx, cache, data = _ring(cfg)
+    segs, outs, qs = [], [], []
+    for i in range(8):
+        q = synth.frame(G, cfg, 1, 7 + i, synth.Q)
+        o = torch.empty((N, G.n_heads, G.head_dim), dtype=torch.bfloat16, device="cuda")
+        qs.append(q)
+        outs.append(o)
+        segs.append(rf.Segment(up(q), 7 + i, o, i, 14))
+    rf.window_attention(ctx, cache, segs)
+    torch.cuda.synchronize()
+    rk = RotatedKeys(G)
+    for i in range(8):
+        rows = sample_rows(N, N, extra=8, seed=20 + i)
+        _check(data, qs[i], 7 + i, outs[i], i, i + 14, rows, 1.0 / np.sqrt(G.head_dim), f"segment {i}", rk)
