@@ -51,6 +51,71 @@ def measured_traffic(flops_per_launch):
     return t.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's effective shader clock (MHz) with amdsmi from a host thread while
+    the timed loop runs: the firmware metrics' current gfx clock of each XCD, averaged
+    over the XCDs (the clock query's `clk` field gives the DPM level, 2,400 MHz, which
+    the chip does not hold under this load).  Read-only queries; None if amdsmi is
+    unavailable."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.ok = False
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+            self.ok = True
+        except Exception:  # no amdsmi, no permission, no device: no clock figure
+            self.ok = False
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        per_xcd = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and v > 0]
+        if per_xcd:
+            return float(np.mean(per_xcd))
+        v = m.get("current_gfxclk")
+        if isinstance(v, (int, float)) and v > 0:
+            return float(v)
+        raise RuntimeError("no gfx clock in the metrics")
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        if self.ok:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self, skip_s=0.0):
+        """Stop sampling; summarise the samples taken after the first skip_s seconds."""
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self.ok:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        vals = [v for v in self.samples[int(skip_s / self.period):] if isinstance(v, (int, float)) and v > 0]
+        if not vals:
+            return None
+        return {"median": float(np.median(vals)), "min": float(min(vals)), "max": float(max(vals)),
+                "samples": len(vals)}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -59,6 +124,8 @@ def parse():
     p.add_argument("--pool", type=int, default=4, help="distinct pre-generated step inputs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle run time")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the untimed ~1.5 s phase that samples the shader clock")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the untimed denoise-only and RoPE launches (profiling runs, so "
                         "that every attention dispatch traced is a batched step)")
@@ -144,6 +211,20 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
+
+    # Shader clock under this load: the firmware metrics refresh too slowly for the
+    # short timed loop, so sample during ~1.5 s of the same steps first (untimed) and
+    # keep the samples of the last second.
+    clock = ClockSampler(period_s=0.005)
+    sclk = None
+    if clock.ok and not args.no_clock:
+        clock.start()
+        t_end_clock = time.perf_counter() + 1.5
+        while time.perf_counter() < t_end_clock:
+            for _ in range(20):
+                run_step()
+            torch.cuda.synchronize()
+        sclk = clock.stop(skip_s=0.5)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -248,6 +329,10 @@ def main():
             "kernel": "window_attn_kernel",
             "flops_per_launch": flops_step,
             "ms_per_launch": round(attn_ms, 4),
+            # peak scales with the shader clock: 2.5 PFLOP/s is quoted at 2,400 MHz
+            "sclk_mhz": sclk,
+            "frac_at_sclk": (round(attn_tflops / (PEAK_BF16_TFLOPS * sclk["median"] / 2400.0), 4)
+                             if sclk else None),
         },
         "ms_attention": round(attn_ms, 4),
         "ms_roll": round(roll_ms, 4),
