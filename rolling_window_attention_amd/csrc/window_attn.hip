@@ -44,7 +44,10 @@
 // score MFMAs of tile j) and a softmax half (weights of tile j; staging of
 // the group's share of the next K/V tiles).  Group 1 runs one half behind
 // group 0, so on every SIMD one wave issues MFMAs while the other does its
-// softmax.  K/V tiles are gathered from the ring slots with raw buffer loads
+// softmax.  (The compiler moves the exponentials of the softmax half down to
+// the start of the next MFMA half, next to the value MFMAs that use them;
+// pinning them in the softmax half measured slower, as the other wave's MFMAs
+// halve a wave's VALU issue rate.)  K/V tiles are gathered from the ring slots with raw buffer loads
 // into registers and written to padded LDS rows (conflict-free 16-byte
 // fragment reads) one step later: a tile inside one frame takes a fixed lane
 // offset plus a scalar base; a tile straddling two frames (or past the
@@ -60,7 +63,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlockM = kAttnBlockM;       // query rows per work item (128)
+constexpr int kBlockM = kAttnBlockM;       // query rows per work item (256)
 constexpr int kBlockN = kAttnBlockN;       // keys per tile (64)
 constexpr int kThreads = 512;              // 8 waves of 32 query rows
 constexpr int kKRow = kHeadDim + 8;        // LDS row stride of K tile (272 B: conflict-free 16 B reads)
