@@ -31,10 +31,16 @@ KERNEL_SOURCES = ["window_attn.hip", "device_common.h", "kernels.h"]
 
 
 def kernel_source_hash():
+    """Hash of the attention kernel's sources without // comments and blank lines, so a
+    comment edit does not invalidate counter figures taken on the same code."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "rolling_window_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "rolling_window_attention_amd", "csrc", name)) as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
