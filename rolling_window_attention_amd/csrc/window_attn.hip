@@ -23,14 +23,29 @@
 //
 // Per query tile: eight waves of 32 query rows (two per SIMD) share each K/V
 // tile, which the work-group fetches and stages once.  Per 64-key tile:
-//   T^T[key][q] = K_tile . Q'^T - m  v_mfma_f32_32x32x16_bf16, 2 key blocks x (8+1) k-steps
+//   T^T[key][q] = K_tile . Q'^T - m  v_mfma_f32_32x32x16_bf16, 2 key blocks x 8 k-steps
 //   online softmax in float32: 2^T, bf16 weights P, row sums
 //   O^T[d][q]  += V^T_tile . P^T     4 dim blocks x 4 k-steps
 // Q' is Q rotated (3D-RoPE) and scaled by scale*log2(e) on load, so the score
-// MFMAs deliver exponents in log2 units; the ninth k-step of each key block
-// subtracts the running row max m (A: 1 in k-slot 0 for every key, B: -m in
-// k-slot 0 for every query).  The softmax is then one exp2, half a pack and
+// MFMAs deliver exponents in log2 units; the running row max m enters as the
+// accumulator input of each key block's first k-step (a register block holding
+// -m for this lane's query).  The softmax is then one exp2, half a pack and
 // half a dot2 per score, plus the tile max.
+//
+// Registers (256 per lane for each of the two waves of a SIMD): the O^T
+// accumulators sit in the fixed accumulation registers a[0:63] and the Q'
+// fragments in 32 further accumulation registers, leaving 160 VGPRs for the
+// scores, the K/V fragments, the weights and the staging.  With O^T out of the
+// VGPR file, the VALU work of the other wave on the SIMD issues more freely
+// next to the value MFMAs.  Those MFMAs are written as inline assembly on
+// a[16dt:16dt+15]; so are the zeroing, the lazy rescale and the final reads of
+// O^T.  The compiler does not see that a[0:63] hold live values, so the
+// library build scans the generated assembly and fails if any instruction
+// outside these statements names a0..a63.  The compiler does not see either
+// that the statements are MFMAs, so they carry their own wait states: two
+// before each MFMA (a VALU-written operand, e.g. the weights P), eighteen or
+// more between the last MFMA writing a register and the first VALU or memory
+// instruction reading it.
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so a row max needs one cross-half exchange, the row sum
 // none until the end, and the rescale is a per-lane scalar.  The key order
@@ -90,7 +105,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ float xhalf_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -113,11 +128,51 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return rem * per + (x - rem) * (per - 1) + idx;
 }
 
-// Round x up to a bf16-representable float (towards +infinity).
-__device__ __forceinline__ float bf16_ceil(float x) {
-  uint32_t b = __float_as_uint(x);
-  if (x > 0.0f) b += 0xFFFFu;
-  return __uint_as_float(b & 0xFFFF0000u);
+// ---- O^T in accumulation registers a[0:63] (block dt in a[16dt:16dt+15]) --------
+#define RF_O_REGS                                                                                                 \
+  "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", "a16", "a17", \
+      "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", "a32", "a33", \
+      "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", "a48", "a49", \
+      "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63"
+#define RF_FOR64(M)                                                                                                \
+  M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7) M(8) M(9) M(10) M(11) M(12) M(13) M(14) M(15) M(16) M(17) M(18) M(19)    \
+  M(20) M(21) M(22) M(23) M(24) M(25) M(26) M(27) M(28) M(29) M(30) M(31) M(32) M(33) M(34) M(35) M(36) M(37)    \
+  M(38) M(39) M(40) M(41) M(42) M(43) M(44) M(45) M(46) M(47) M(48) M(49) M(50) M(51) M(52) M(53) M(54) M(55)    \
+  M(56) M(57) M(58) M(59) M(60) M(61) M(62) M(63)
+#define RF_ZERO1(n) "v_accvgpr_write_b32 a" #n ", 0\n\t"
+#define RF_SCALE1(n) "v_accvgpr_read_b32 %0, a" #n "\n\tv_mul_f32 %0, %0, %1\n\tv_accvgpr_write_b32 a" #n ", %0\n\t"
+#define RF_RD1(i, n) "v_accvgpr_read_b32 %" #i ", a" #n "\n\t"
+#define RF_RD16(n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13, n14, n15)                          \
+  RF_RD1(0, n0) RF_RD1(1, n1) RF_RD1(2, n2) RF_RD1(3, n3) RF_RD1(4, n4) RF_RD1(5, n5) RF_RD1(6, n6) RF_RD1(7, n7) \
+      RF_RD1(8, n8) RF_RD1(9, n9) RF_RD1(10, n10) RF_RD1(11, n11) RF_RD1(12, n12) RF_RD1(13, n13) RF_RD1(14, n14) \
+          RF_RD1(15, n15)
+#define RF_OUT16(r)                                                                                               \
+  "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]), "=v"(r[8]),     \
+      "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15])
+
+// O^T block dt += A . B (A: 32 dims x 16 keys of V^T, B: 16 keys x 32 queries of
+// P^T); s_nop 1 covers a B operand written by the VALU just before.
+template <int DT>
+__device__ __forceinline__ void mfma_o(bf16x8 a, u32x4 b);
+template <>
+__device__ __forceinline__ void mfma_o<0>(bf16x8 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]" ::"v"(a), "v"(b)
+               : "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15");
+}
+template <>
+__device__ __forceinline__ void mfma_o<1>(bf16x8 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(a), "v"(b)
+               : "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31");
+}
+template <>
+__device__ __forceinline__ void mfma_o<2>(bf16x8 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(a), "v"(b)
+               : "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47");
+}
+template <>
+__device__ __forceinline__ void mfma_o<3>(bf16x8 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(a), "v"(b)
+               : "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63");
 }
 
 // One work item: query tile qt of head h of segment sg, key tiles [ka, kb).
@@ -282,20 +337,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   };
 
   // ---- running state -----------------------------------------------------------
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-  // Running row max m (log2 units), kept bf16-representable: the score MFMAs
-  // subtract it themselves through one more k-step whose A operand is 1 in
-  // k-slot 0 (all keys) and whose B operand is -m in k-slot 0 (per query).
+  asm volatile(RF_FOR64(RF_ZERO1) ::: RF_O_REGS);  // O^T = 0
+  // Running row max m (log2 units).  The score MFMAs subtract it themselves:
+  // the first k-step of each key block accumulates onto negm, -m in all 16
+  // entries (every entry of a lane's accumulator belongs to its query).
   float m_run = 0.0f;
   float l_run = 0.0f;  // this lane's partial row sum of the bf16 weights
-  const u32x4 ones_a = {hf == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
-  u32x4 negm_b = {0u, 0u, 0u, 0u};
+  f32x16 negm = {};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const f32x16 zero16 = {};
 
   // A-operand row m of the score MFMA reads key kappa(m): lane half hf of
   // output register i then holds key 16*hf + i of each 32-key block.
@@ -305,13 +354,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   // (Q' = c Q): the exponents of the softmax weights in log2 units.  All 16
   // K fragments are read before the first MFMA (sched_barrier keeps the
   // compiler from sinking the reads next to their MFMAs), so LDS latency is
-  // paid once per block.
+  // paid once per block.  The Q' fragments are B operands taken from
+  // accumulation registers.  Eight statements of two MFMAs each let every
+  // pair start as soon as its two fragments have arrived; the last one waits
+  // out the MFMA latency before the softmax reads the scores.
   // Both MFMA blocks run at raised wave priority.
   auto scores = [&](int buf, f32x16& s0, f32x16& s1) {
     const uint16_t* Kl = lds + buf * kKTile;
     __builtin_amdgcn_s_setprio(1);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones_a), as_bf16x8(negm_b), zero16, 0, 0, 0);
     bf16x8 kf[16];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -319,28 +369,48 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
       kf[2 * s + 1] = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * s], qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * s + 1], qf[s], s1, 0, 0, 0);
-    }
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %5, %4\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %5, %4"
+                 : "=&v"(s0), "=&v"(s1)
+                 : "v"(kf[0]), "v"(kf[1]), "v"(negm), "a"(qf[0]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[2]), "v"(kf[3]), "a"(qf[1]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[4]), "v"(kf[5]), "a"(qf[2]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[6]), "v"(kf[7]), "a"(qf[3]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[8]), "v"(kf[9]), "a"(qf[4]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[10]), "v"(kf[11]), "a"(qf[5]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[12]), "v"(kf[13]), "a"(qf[6]));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %4, %1\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+v"(s0), "+v"(s1)
+                 : "v"(kf[14]), "v"(kf[15]), "a"(qf[7]));
     __builtin_amdgcn_s_setprio(0);
   };
 
   // Row max of a tile's exponents (both lane halves).
   auto tile_max = [&](const f32x16& s0, const f32x16& s1) -> float {
-    float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
+    // two chains of 3-input maxima
+    float ma = __builtin_elementwise_maximum(s0[0], s0[1]);
+    float mb = __builtin_elementwise_maximum(s1[0], s1[1]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2)
-      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s0[i + 1]));
-#pragma unroll
-    for (int i = 0; i < 16; i += 2)
-      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s1[i], s1[i + 1]));
-    return xhalf_max(mx);
+    for (int i = 2; i < 16; i += 2) {
+      ma = __builtin_elementwise_maximum(__builtin_elementwise_maximum(ma, s0[i]), s0[i + 1]);
+      mb = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mb, s1[i]), s1[i + 1]);
+    }
+    return xhalf_max(__builtin_elementwise_maximum(ma, mb));
   };
 
-  // Move the running max up by delta (bf16-representable m_new - m_run > 0):
-  // shift this tile's exponents, rescale l and O, refresh -m for the MFMAs.
+  // Move the running max up to m_new: shift this tile's exponents, rescale l
+  // and O^T (in its accumulation registers), refresh -m for the MFMAs.
   auto raise_max = [&](float m_new, f32x16& s0, f32x16& s1) {
     const float delta = m_new - m_run;
 #pragma unroll
@@ -350,12 +420,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     }
     const float alpha = __builtin_amdgcn_exp2f(-delta);
     l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    float t;
+    asm volatile(RF_FOR64(RF_SCALE1) : "=&v"(t) : "v"(alpha) : RF_O_REGS);
     m_run = m_new;
-    negm_b[0] = hf == 0 ? (__float_as_uint(-m_new) >> 16) : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m_new;
   };
 
   // Online softmax of one tile: the running max only moves when some row's
@@ -364,7 +433,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   auto softmax = [&](f32x16& s0, f32x16& s1, u32x4 (&pw)[4]) {
     const float mt = tile_max(s0, s1);
     if (__builtin_amdgcn_ballot_w64(mt > kRescaleLog2) != 0)
-      raise_max(bf16_ceil(m_run + fmaxf(mt, 0.0f)), s0, s1);
+      raise_max(m_run + fmaxf(mt, 0.0f), s0, s1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float a0 = __builtin_amdgcn_exp2f(s0[2 * e]);
@@ -391,10 +460,12 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
         vf[4 * dt + bu] = *(const bf16x8*)(Vl + (32 * dt + lr) * kVRow + 32 * (bu >> 1) + 16 * hf + 8 * (bu & 1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int bu = 0; bu < 4; ++bu)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * dt + bu], as_bf16x8(pw[bu]), o[dt], 0, 0, 0);
+    for (int bu = 0; bu < 4; ++bu) {
+      mfma_o<0>(vf[bu], pw[bu]);
+      mfma_o<1>(vf[4 + bu], pw[bu]);
+      mfma_o<2>(vf[8 + bu], pw[bu]);
+      mfma_o<3>(vf[12 + bu], pw[bu]);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -439,15 +510,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     scores(j & 1, x0, x1);
     __syncthreads();
     if (j == ntiles - 1) mask_tail(kb - 1, x0, x1);
-    if (j == 0) {  // first tile: the running max starts at its (rounded up) row max
-      const float m0 = bf16_ceil(tile_max(x0, x1));
+    if (j == 0) {  // first tile: the running max starts at its row max
+      const float m0 = tile_max(x0, x1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x0[i] -= m0;
         x1[i] -= m0;
       }
       m_run = m0;
-      negm_b[0] = hf == 0 ? (__float_as_uint(-m0) >> 16) : 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m0;
     }
     softmax(x0, x1, pw);
     store_k((j + 1 + grp) & 1);
@@ -458,6 +530,21 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   }
   values((ntiles - 1) & 1, pw);
   if (grp == 0) __syncthreads();  // the same barrier count as group 1
+
+  // O^T out of the accumulation registers, once the last MFMAs have drained.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: RF_O_REGS);
+  f32x16 o[4];
+  {
+    float r[4][16];
+    asm volatile(RF_RD16(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15) : RF_OUT16(r[0]));
+    asm volatile(RF_RD16(16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31) : RF_OUT16(r[1]));
+    asm volatile(RF_RD16(32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43, 44, 45, 46, 47) : RF_OUT16(r[2]));
+    asm volatile(RF_RD16(48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63) : RF_OUT16(r[3]));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = r[dt][i];
+  }
 
   // ---- epilogue --------------------------------------------------------------------
   const float l_tot = xhalf_sum(l_run);
