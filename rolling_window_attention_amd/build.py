@@ -18,10 +18,17 @@ halves the file (128 + 128) once a kernel uses accumulation registers:
 The attention kernels keep the output accumulators in the fixed accumulation
 registers a0..a63, written and read only by inline assembly, which the register
 allocator does not know about.  The generated assembly is therefore checked
-before it is assembled: no other instruction of those kernels may name a0..a63,
-and the kernels must be granted at least 64 accumulation registers.  The whole
-file is also checked for packed-fp32 VALU instructions, which the build
-disables.
+before it is assembled:
+  * no other instruction of those kernels may name a0..a63, and the kernels
+    must be granted at least 64 accumulation registers;
+  * their MFMAs are inline assembly, so the compiler's hazard recognizer does
+    not see them: a scan over the control-flow graph requires at least 12 wait
+    states (instructions issued, s_nop n counting n+1) between an MFMA writing
+    a register and any non-MFMA instruction touching it or an MFMA taking it as
+    an A/B operand (12 is what the compiler itself inserts for these MFMAs),
+    and 2 between a VALU write and an MFMA reading the register;
+  * the whole file has no packed-fp32 VALU instructions, which the build
+    disables.
 """
 import os
 import re
@@ -104,10 +111,100 @@ def set_agpr_alloc(ll_text, n):
     return "\n".join(out)
 
 
+MFMA_RESULT_WAIT = 12   # MFMA writes a register -> another instruction touches it
+VALU_TO_MFMA_WAIT = 2   # VALU writes a register -> an MFMA reads it
+_NO_VDST = ("v_cmp", "v_readlane", "v_readfirstlane", "s_", "ds_write", "buffer_store", "global_store",
+            "scratch_store", "flat_store")
+
+
+def _vregs(tok):
+    """Vector registers named by one operand: v5, v[4:7], a3, a[0:3]."""
+    tok = tok.split()[0] if tok else tok
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return [f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)]
+    return [tok] if re.fullmatch(r"[va]\d+", tok) else []
+
+
+def mfma_hazards(fn_lines, name):
+    """Wait-state hazards around MFMAs in one function's assembly (see module doc)."""
+    blocks, cur, lab = [], [], "entry"
+    for line in fn_lines:
+        code = line.split(";")[0].strip()
+        m = re.match(r"^(\.?[\w$.]+):$", code)
+        if m:
+            blocks.append((lab, cur))
+            cur, lab = [], m.group(1)
+            continue
+        if not code or code.startswith("."):
+            continue
+        parts = code.split(None, 1)
+        ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+        cur.append((parts[0], ops))
+        if parts[0].startswith("s_cbranch") or parts[0] == "s_branch":  # a branch ends a block
+            blocks.append((lab, cur))
+            cur, lab = [], f"{lab}+{len(blocks)}"
+    blocks.append((lab, cur))
+    index = {b[0]: i for i, b in enumerate(blocks)}
+    succ = []
+    for i, (_, ins) in enumerate(blocks):
+        s = [index[o[0]] for mn, o in ins if (mn.startswith("s_cbranch") or mn == "s_branch") and o and o[0] in index]
+        last = ins[-1][0] if ins else ""
+        if last not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(blocks):
+            s.append(i + 1)
+        succ.append(s)
+    state = [None] * len(blocks)
+    state[0] = ({}, {})
+    work, problems = [0], set()
+    while work:
+        b = work.pop()
+        mf, vw = dict(state[b][0]), dict(state[b][1])
+        for mn, ops in blocks[b][1]:
+            if mn.startswith("v_mfma"):
+                for k, op in enumerate(ops[1:4]):
+                    for r in _vregs(op):
+                        if mf.get(r, 0) > 0 and k != 2:  # the C operand is interlocked in hardware
+                            problems.add(f"{name}: {mn} takes MFMA result {r} as an A/B operand too early")
+                        if vw.get(r, 0) > 0:
+                            problems.add(f"{name}: {mn} reads VALU-written {r} too early")
+            elif not mn.startswith("s_"):
+                for op in ops:
+                    for r in _vregs(op):
+                        if mf.get(r, 0) > 0:
+                            problems.add(f"{name}: {mn} {', '.join(ops)} touches MFMA result {r} too early")
+            w = int(ops[0], 0) + 1 if mn == "s_nop" else 1
+            for d in (mf, vw):
+                for r in list(d):
+                    d[r] -= w
+                    if d[r] <= 0:
+                        del d[r]
+            if mn.startswith("v_mfma"):
+                for r in _vregs(ops[0]):
+                    mf[r] = MFMA_RESULT_WAIT
+            elif mn.startswith("v_") and ops and not mn.startswith(_NO_VDST):
+                for r in _vregs(ops[0]):
+                    vw[r] = VALU_TO_MFMA_WAIT
+        for t in succ[b]:
+            if state[t] is None:
+                state[t] = (dict(mf), dict(vw))
+                work.append(t)
+                continue
+            changed = False
+            for old, new in zip(state[t], (mf, vw)):
+                for r, x in new.items():
+                    if old.get(r, 0) < x:
+                        old[r] = x
+                        changed = True
+            if changed:
+                work.append(t)
+    return sorted(problems)
+
+
 def check_attention_asm(asm_text):
     """Raise if the compiler touched a0..a63 in the attention kernels, if those
-    kernels were granted fewer than 64 accumulation registers, or if any
-    packed-fp32 VALU instruction was emitted."""
+    kernels were granted fewer than 64 accumulation registers, if an MFMA
+    hazard is not covered by enough wait states, or if any packed-fp32 VALU
+    instruction was emitted."""
     problems = []
     fn, in_asm, seen = None, False, set()
     for line in asm_text.split("\n"):
@@ -138,6 +235,21 @@ def check_attention_asm(asm_text):
                 problems.append(f"compiler-generated use of a{r} in {fn}: {code}")
     if not seen:
         problems.append("attention kernels not found in the generated assembly")
+    # wait-state hazards around the MFMAs, per attention kernel
+    fns, name = {}, None
+    for line in asm_text.split("\n"):
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name = m.group(1) if m.group(1).startswith(ATTN_KERNEL_PREFIX) else None
+            if name:
+                fns[name] = []
+            continue
+        if name and line.startswith(".Lfunc_end"):
+            name = None
+        elif name:
+            fns[name].append(line)
+    for fname, body in fns.items():
+        problems += mfma_hazards(body, fname)
     # kernel descriptors: accumulation registers = next_free_vgpr - accum_offset
     for name, body in re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", asm_text, re.S):
         if not name.startswith(ATTN_KERNEL_PREFIX):

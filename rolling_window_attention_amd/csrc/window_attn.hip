@@ -43,9 +43,12 @@
 // library build scans the generated assembly and fails if any instruction
 // outside these statements names a0..a63.  The compiler does not see either
 // that the statements are MFMAs, so they carry their own wait states: two
-// before each MFMA (a VALU-written operand, e.g. the weights P), eighteen or
-// more between the last MFMA writing a register and the first VALU or memory
-// instruction reading it.
+// before an MFMA whose operand the VALU may just have written (the weights P,
+// -m), eighteen or more between the last MFMA writing a register and the first
+// VALU or memory instruction touching it.  The build also scans the generated
+// assembly for any instruction (its own or the compiler's) that touches an
+// MFMA result, or feeds an MFMA a VALU result, with fewer wait states than
+// those two rules require.
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so a row max needs one cross-half exchange, the row sum
 // none until the end, and the rescale is a per-lane scalar.  The key order
@@ -151,7 +154,9 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
       "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15])
 
 // O^T block dt += A . B (A: 32 dims x 16 keys of V^T, B: 16 keys x 32 queries of
-// P^T); s_nop 1 covers a B operand written by the VALU just before.
+// P^T).  The four blocks of one 16-key group take the same B operand in the order
+// dt = 0..3; the s_nop 1 before the first covers a B operand written by the VALU
+// just before (the next three read it after that first MFMA has issued).
 template <int DT>
 __device__ __forceinline__ void mfma_o(bf16x8 a, u32x4 b);
 template <>
@@ -161,17 +166,17 @@ __device__ __forceinline__ void mfma_o<0>(bf16x8 a, u32x4 b) {
 }
 template <>
 __device__ __forceinline__ void mfma_o<1>(bf16x8 a, u32x4 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(a), "v"(b)
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(a), "v"(b)
                : "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31");
 }
 template <>
 __device__ __forceinline__ void mfma_o<2>(bf16x8 a, u32x4 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(a), "v"(b)
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(a), "v"(b)
                : "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47");
 }
 template <>
 __device__ __forceinline__ void mfma_o<3>(bf16x8 a, u32x4 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(a), "v"(b)
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(a), "v"(b)
                : "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63");
 }
 

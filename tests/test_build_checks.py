@@ -29,7 +29,8 @@ def _asm(body, nfv=256, acc=160, kernel=K):
 
 
 def test_clean_kernel_passes():
-    B.check_attention_asm(_asm("\tv_accvgpr_write_b32 a64, v1\n\tv_mfma_f32_32x32x16_bf16 v[0:15], v[2:5], a[64:67], v[0:15]"))
+    B.check_attention_asm(_asm("\tv_accvgpr_write_b32 a64, v1\n\ts_nop 1\n"
+                               "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[2:5], a[64:67], v[0:15]"))
 
 
 @pytest.mark.parametrize("body", [
@@ -68,3 +69,39 @@ def test_agpr_alloc_attribute_edit():
     out = B.set_agpr_alloc(ll, 96)
     assert 'attributes #2 = { "amdgpu-agpr-alloc"="96" convergent }' in out
     assert 'attributes #0 = { "amdgpu-agpr-alloc"="0" nounwind }' in out
+
+
+# ---- wait-state hazards around inline-assembly MFMAs ---------------------------------
+MF = "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"
+
+
+def _hz(body):
+    return B.mfma_hazards(body.split("\n"), "k")
+
+
+def test_reading_an_mfma_result_too_early_is_rejected():
+    assert _hz(MF + "\n\tv_mov_b32 v30, v3")                            # right after
+    assert _hz(MF + "\n\ts_nop 7\n\tv_max3_f32 v30, v1, v2, v3")        # 9 wait states
+    assert not _hz(MF + "\n\ts_nop 7\n\ts_nop 3\n\tv_mov_b32 v30, v3")  # 13
+    assert not _hz(MF + "\n\tv_mov_b32 v30, v40")                       # other registers
+
+
+def test_mfma_chains_and_valu_to_mfma():
+    # accumulating into the same registers: interlocked
+    assert not _hz(MF + "\n" + MF)
+    # an MFMA result as the A operand of the next MFMA: hazard
+    assert _hz(MF + "\n\tv_mfma_f32_32x32x16_bf16 v[40:55], v[0:3], v[20:23], v[40:55]")
+    # VALU write feeding an MFMA operand needs two wait states
+    assert _hz("\tv_cvt_pk_bf16_f32 v20, v1, v2\n" + MF)
+    assert not _hz("\tv_cvt_pk_bf16_f32 v20, v1, v2\n\ts_nop 1\n" + MF)
+
+
+def test_hazard_across_a_branch_is_found():
+    body = MF + "\n\ts_cbranch_scc1 .LBB0_2\n\ts_nop 7\n\ts_nop 7\n.LBB0_2:\n\tv_mov_b32 v30, v5"
+    assert _hz(body)  # the taken path reaches the read without the s_nops
+
+
+def test_check_attention_asm_reports_hazards():
+    with pytest.raises(RuntimeError):
+        B.check_attention_asm(_asm("\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], a[64:67], v[0:15]\n"
+                                   "\tv_max3_f32 v30, v1, v2, v3"))
