@@ -27,18 +27,20 @@ METRIC = "attention TFLOP/s + ms/layer at 23,400q x 32,760kv x 12h; % bf16 MFMA 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_attn_traffic.json")
-KERNEL_SOURCES = ["window_attn.hip", "device_common.h", "kernels.h"]
+KERNEL_SOURCES = ["csrc/window_attn.hip", "csrc/device_common.h", "csrc/kernels.h", "build.py"]
 
 
 def kernel_source_hash():
-    """Hash of the attention kernel's sources without // comments and blank lines, so a
-    comment edit does not invalidate counter figures taken on the same code."""
+    """Hash of what the attention kernel is made from (its sources and the build script,
+    which sets its register split) without comments and blank lines, so a comment edit
+    does not invalidate counter figures taken on the same code."""
     import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "rolling_window_attention_amd", "csrc", name)) as f:
+        comment = r"#.*" if name.endswith(".py") else r"//.*"
+        with open(os.path.join(ROOT, "rolling_window_attention_amd", name)) as f:
             for line in f:
-                code = re.sub(r"//.*", "", line).rstrip()
+                code = re.sub(comment, "", line).rstrip()
                 if code:
                     h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
