@@ -98,6 +98,40 @@ __device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, int p0, int64_t t, i
   return y;
 }
 
+// (cos, sin) of the 4 rotation pairs p0..p0+3 of a token at (t, r, c), widened
+// to float64 (exactly), for rope_chunk_cs.
+struct ChunkCS {
+  double c[4], s[4];
+};
+__device__ __forceinline__ ChunkCS rope_chunk_cs_of(const RopeTables& T, int p0, int64_t t, int r, int c) {
+  ChunkCS out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 cs = rope_cs(T, p0 + k, t, r, c);
+    out.c[k] = (double)cs.x;
+    out.s[k] = (double)cs.y;
+  }
+  return out;
+}
+
+// rope_chunk with the chunk's (cos, sin) given: the same arithmetic, so the
+// same bits, when several chunks share the pairs and the position (the heads
+// of one token).
+__device__ __forceinline__ u32x4 rope_chunk_cs(u32x4 x, const ChunkCS& cs) {
+  uint32_t in[4] = {x[0], x[1], x[2], x[3]};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    double x0 = (double)bf16_to_f32(in[k] & 0xFFFFu);
+    double x1 = (double)bf16_to_f32(in[k] >> 16);
+    double y0 = x0 * cs.c[k] - x1 * cs.s[k];
+    double y1 = x0 * cs.s[k] + x1 * cs.c[k];
+    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+  }
+  u32x4 y = {out[0], out[1], out[2], out[3]};
+  return y;
+}
+
 // Exact unsigned division n / d for n < 2^24, d >= 1: a float estimate is off
 // by at most one and is corrected with one multiply-subtract.
 __device__ __forceinline__ uint32_t small_div(uint32_t n, uint32_t d, float inv_d, uint32_t* rem) {

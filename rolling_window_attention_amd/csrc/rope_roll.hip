@@ -12,28 +12,26 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef RF_ROPE_BATCH
+#define RF_ROPE_BATCH 3
+#endif
+#ifndef RF_ROPE_HPT
+#define RF_ROPE_HPT 3
+#endif
+#ifndef RF_V_BLOCK
+#define RF_V_BLOCK 128
+#endif
+
 namespace rfattn {
 
-// rope3d works on 16-byte chunks (8 bf16, 4 rotation pairs) spread over the
-// threads of a work-group: on gfx950 a streaming kernel reaches copy
-// bandwidth with one or two loads per thread in flight and many waves, and
-// loses it (down to ~60%) when a thread batches eight loads before its
-// stores.
-
-// Position of chunk q of a token-major [tokens][H*16 chunks] range: the
-// work-group's first token is found once (uniform division), the thread's
-// token by a small exact division of its offset from there.
-struct ChunkPos {
-  uint32_t tok;   // token index in the range
-  uint32_t hc;    // head * 16 + chunk
-};
-__device__ __forceinline__ ChunkPos chunk_pos(uint32_t blk_base, uint32_t row_chunks, float inv_row) {
-  const uint32_t tok0 = __builtin_amdgcn_readfirstlane(blk_base / row_chunks);
-  const uint32_t rem0 = blk_base - tok0 * row_chunks;
-  uint32_t hc;
-  const uint32_t tl = small_div(rem0 + threadIdx.x, row_chunks, inv_row, &hc);
-  return {tok0 + tl, hc};
-}
+// Both kernels rotate 16-byte chunks (8 bf16, 4 rotation pairs).  A thread owns
+// one chunk column c (pairs 4c..4c+3) of one token and a group of kRopeHpt of the
+// token's heads: the pairs' (cos, sin), their table lookups and float64 widening
+// are shared by the group, which leaves the rotation itself as the thread's
+// arithmetic.  A work-group is 16 (token, head group) rows x 16 columns, so each
+// load or store instruction of a wave covers four 256-byte head rows.  Three
+// heads per thread with all three loads in flight measured fastest: more heads
+// per thread leave too few threads, fewer repeat the shared work.
 
 // (frame offset, row, column) of token `tok` of a range whose token 0 starts
 // frame 0; frames have N tokens of gw columns.
@@ -47,46 +45,53 @@ __device__ __forceinline__ TokPos tok_pos(uint32_t tok, uint32_t N, float inv_n,
   return {f, row, col};
 }
 
-// ---------------------------------------------------------------------------
-// rope3d: thread = one chunk of the [n_tokens][H*16] range.
-// ---------------------------------------------------------------------------
 constexpr int kRopeThreads = 256;
+constexpr int kRopeRows = kRopeThreads / 16;     // (token, head group) rows per work-group
+constexpr int kRopeHpt = RF_ROPE_HPT;            // heads per thread (a head group)
+constexpr int kRopeBatch = RF_ROPE_BATCH;        // head chunks loaded before the first is rotated
 
-// Tokens [tok_base, tok_base + n) of the range, n * H * 16 < 2^31.  A
-// work-group covers kRopeU * 256 consecutive chunks; thread t takes chunks
-// t, t + 256, ...: all its loads are issued first, so each wave keeps kRopeU
-// loads in flight while it does the float64 rotation of the earlier ones.
-constexpr int kRopeU = 2;
-__global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a, uint32_t tok_base, uint32_t n) {
-  const uint32_t row_chunks = (uint32_t)a.H * 16u;
-  const float inv_row = 1.0f / (float)row_chunks;
-  u32x4 x[kRopeU];
-  ChunkPos cp[kRopeU];
+// Row R of the [tokens][head groups] grid -> token and the group's first head.
+__device__ __forceinline__ void rope_row(uint32_t R, int H, uint32_t* tok, int* h0) {
+  const uint32_t ng = (uint32_t)((H + kRopeHpt - 1) / kRopeHpt);
+  *tok = R / ng;
+  *h0 = (int)(R - *tok * ng) * kRopeHpt;
+}
+
+// Heads [h0, h1) of one (token, column): y[h] = RoPE(x[h]), kRopeBatch loads in
+// flight.  Element offset of head h's chunk: base + h * 128.
+template <typename Store>
+__device__ __forceinline__ void rotate_heads(const uint16_t* x, int h0, int h1, const ChunkCS& cs, Store store) {
+  for (int hb = h0; hb < h1; hb += kRopeBatch) {
+    u32x4 v[kRopeBatch];
 #pragma unroll
-  for (int u = 0; u < kRopeU; ++u) {
-    const uint32_t base = (blockIdx.x * (uint32_t)kRopeU + u) * (uint32_t)kRopeThreads;
-    cp[u] = chunk_pos(base, row_chunks, inv_row);
-    if (cp[u].tok < n) {
-      const uint32_t tok = tok_base + cp[u].tok;
-      x[u] = __builtin_nontemporal_load(
-          (const u32x4*)(a.x + (int64_t)tok * a.x_ld + (int64_t)(cp[u].hc >> 4) * 128 + (cp[u].hc & 15u) * 8));
-    }
-  }
+    for (int u = 0; u < kRopeBatch; ++u)
+      if (hb + u < h1) v[u] = __builtin_nontemporal_load((const u32x4*)(x + (hb + u) * 128));
 #pragma unroll
-  for (int u = 0; u < kRopeU; ++u) {
-    if (cp[u].tok >= n) continue;
-    const uint32_t tok = tok_base + cp[u].tok;
-    const uint32_t c = cp[u].hc & 15u;
-    const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
-    const u32x4 y = rope_chunk(x[u], (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col, a.tab);
-    __builtin_nontemporal_store(y, (u32x4*)(a.y + (int64_t)tok * a.y_ld + (int64_t)(cp[u].hc >> 4) * 128 + c * 8));
+    for (int u = 0; u < kRopeBatch; ++u)
+      if (hb + u < h1) store(hb + u, rope_chunk_cs(v[u], cs));
   }
 }
 
 // ---------------------------------------------------------------------------
-// roll: a thread owns an 8-token x 8-dim block of one (frame, head) of the
-// keys (grid z = 0) or of the values (z = 1).
-// Keys: 8 rows of 16 bytes are read, rotated, written to K[slot][h][n][d].
+// rope3d: tokens [tok_base, tok_base + n) of the range; thread = (token, column).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a, uint32_t tok_base, uint32_t n) {
+  uint32_t tl;
+  int h0;
+  rope_row(blockIdx.x * (uint32_t)kRopeRows + (threadIdx.x >> 4), a.H, &tl, &h0);
+  const uint32_t c = threadIdx.x & 15u;
+  if (tl >= n) return;
+  const uint32_t tok = tok_base + tl;
+  const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
+  const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col);
+  uint16_t* yrow = a.y + (int64_t)tok * a.y_ld + c * 8;
+  rotate_heads(a.x + (int64_t)tok * a.x_ld + c * 8, h0, min(h0 + kRopeHpt, a.H), cs,
+               [&](int h, u32x4 y) { __builtin_nontemporal_store(y, (u32x4*)(yrow + h * 128)); });
+}
+
+// ---------------------------------------------------------------------------
+// roll: key work-groups rotate like rope3d and store head-major; value
+// work-groups give a thread an 8-token x 8-dim block of one (frame, head).
 // Values: the 8x8 bf16 block is transposed in registers and written as 8
 // rows of 16 bytes to V[slot][h][d][n] -- the transpose costs no extra pass.
 // Lane layout inside a wave: lane = 8*cc + gg, gg = token group, cc = dim
@@ -113,81 +118,86 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   for (int i = 0; i < 8; ++i) { u32x4 r = {o[i][0], o[i][1], o[i][2], o[i][3]}; out[i] = r; }
 }
 
-// Work-groups [0, k_blocks): keys of tokens [tok_base, tok_base + k_tokens)
-// (k_tokens * H * 16 < 2^31), kRopeU chunks per thread as in rope3d, rotated
-// and stored to K[slot][h][n][d].  Work-groups from k_blocks on: value blocks,
-// a thread per 8 tokens x 8 dims of one (frame, head), transposed in registers
-// and stored to V[slot][h][d][n]; lane = 8*cc + gg (token group gg, dim chunk
-// cc), so every load and store instruction touches 8 runs of 128 bytes.
-__global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t k_blocks, uint32_t tok_base,
+// Values: a value work-group owns (frame, head, 64-dim half, block of kVBlock
+// tokens).  Each thread loads 8 tokens x 8 dims (every load instruction of a
+// wave reads whole 128-byte lines, one per token), transposes them in
+// registers and writes the result into an LDS image [dim][token] of the block;
+// then every dim row of the block leaves as one run of 2 * kVBlock bytes.
+// Measured against the register transpose stored directly (8 runs of 128 bytes
+// per store instruction, none line-aligned since a row is 2N = 3120 bytes for
+// N = 1560): 65 instead of 69 us for the 16-frame roll.  Work-groups owning
+// fewer dims per token read partial lines that a work-group on another XCD
+// fetches again, which measured much slower.
+constexpr int kVBlock = RF_V_BLOCK;  // tokens per value work-group (multiple of 8)
+static_assert(kVBlock % 8 == 0, "value block");
+
+// Work-groups [0, v_blocks): value blocks as above.  Work-groups from v_blocks
+// on: keys of tokens [tok_base, tok_base + k_tokens), a thread per (token, head
+// group, 16-byte column) as in rope3d, rotated and stored to K[slot][h][n][d].
+// The longer value work-groups come first so that they do not form a tail.
+__global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks, uint32_t tok_base,
                                                    uint32_t k_tokens) {
-  if (blockIdx.x < k_blocks) {
-    const uint32_t row_chunks = (uint32_t)a.H * 16u;
-    const float inv_row = 1.0f / (float)row_chunks;
-    u32x4 x[kRopeU];
-    ChunkPos cp[kRopeU];
-#pragma unroll
-    for (int u = 0; u < kRopeU; ++u) {
-      const uint32_t base = (blockIdx.x * (uint32_t)kRopeU + u) * 256u;
-      cp[u] = chunk_pos(base, row_chunks, inv_row);
-      if (cp[u].tok < k_tokens)
-        x[u] = __builtin_nontemporal_load((const u32x4*)(a.k_new + (int64_t)(tok_base + cp[u].tok) * a.k_ld +
-                                                         (int64_t)(cp[u].hc >> 4) * 128 + (cp[u].hc & 15u) * 8));
-    }
-#pragma unroll
-    for (int u = 0; u < kRopeU; ++u) {
-      if (cp[u].tok >= k_tokens) continue;
-      const uint32_t tok = tok_base + cp[u].tok;
-      const uint32_t h = cp[u].hc >> 4, c = cp[u].hc & 15u;
-      const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
-      int slot = a.slot0 + (int)p.f;
-      if (slot >= a.W) slot -= a.W;  // slot0 < W and f < W
-      const u32x4 y = rope_chunk(x[u], (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col, a.tab);
-      const uint32_t n = tok - p.f * (uint32_t)a.N;
-      __builtin_nontemporal_store(
-          y, (u32x4*)(a.k_ring + (int64_t)slot * a.slot_elems + ((int64_t)h * a.N + n) * 128 + c * 8));
-    }
+  if (blockIdx.x >= v_blocks) {
+    uint32_t tl;
+    int h0;
+    rope_row((blockIdx.x - v_blocks) * (uint32_t)kRopeRows + (threadIdx.x >> 4), a.H, &tl, &h0);
+    const uint32_t c = threadIdx.x & 15u;
+    if (tl >= k_tokens) return;
+    const uint32_t tok = tok_base + tl;
+    const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
+    int slot = a.slot0 + (int)p.f;
+    if (slot >= a.W) slot -= a.W;  // slot0 < W and f < W
+    const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col);
+    const uint32_t n = tok - p.f * (uint32_t)a.N;
+    uint16_t* krow = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)n * 128 + c * 8;  // head 0
+    const int64_t head_stride = (int64_t)a.N * 128;
+    rotate_heads(a.k_new + (int64_t)tok * a.k_ld + c * 8, h0, min(h0 + kRopeHpt, a.H), cs, [&](int h, u32x4 y) {
+      __builtin_nontemporal_store(y, (u32x4*)(krow + h * head_stride));
+    });
     return;
   }
-  // value blocks: (frame, head) major, then 8-group blocks of 128 threads
-  const uint32_t groups = (uint32_t)a.N >> 3;
-  const uint32_t vb_per_fh = (((groups + 7) / 8) * 128 + 255) / 256;  // work-groups per (frame, head)
-  const uint32_t vb = blockIdx.x - k_blocks;
-  const uint32_t fh = vb / vb_per_fh;
-  const uint32_t L = (vb - fh * vb_per_fh) * 256u + threadIdx.x;
-  const uint32_t gblock = L >> 7;           // 128 threads per 8 token groups x 16 chunks
-  const uint32_t chalf = (L >> 6) & 1u;
-  const uint32_t cc = (L >> 3) & 7u;
-  const uint32_t gg = L & 7u;
-  const uint32_t g = gblock * 8u + gg;      // token group (8 tokens)
-  const uint32_t c = chalf * 8u + cc;       // dim chunk (8 dims)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kVBlock + 8];
+  const uint32_t N = (uint32_t)a.N;
+  const uint32_t nblk = (N + kVBlock - 1) / kVBlock;
+  const uint32_t fhd = blockIdx.x / nblk;  // (frame, head, half)
+  const uint32_t b = blockIdx.x - fhd * nblk;
+  const uint32_t fh = fhd >> 1, dh = fhd & 1u;
   const int f = (int)fh / a.H;
   const int h = (int)fh - f * a.H;
-  if (g >= groups) return;
   int slot = a.slot0 + f;
   if (slot >= a.W) slot -= a.W;
-  const uint32_t n0 = g * 8u;
-  const int64_t in_tok0 = (int64_t)f * a.N + n0;
-  u32x4 in[8];
+  const uint32_t t0 = b * (uint32_t)kVBlock;
+  const uint32_t ng = (min((uint32_t)kVBlock, N - t0)) >> 3;  // 8-token groups in the block
+  const uint16_t* vin = a.v_new + ((int64_t)f * N + t0) * a.v_ld + h * 128 + dh * 64;
+  for (uint32_t t = threadIdx.x; t < ng * 8; t += 256) {  // (group, 8-dim chunk)
+    const uint32_t c = t & 7u, g = t >> 3;
+    u32x4 in[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    in[j] = __builtin_nontemporal_load((const u32x4*)(a.v_new + (in_tok0 + j) * a.v_ld + h * 128 + c * 8));
-  u32x4 vt[8];
-  transpose8x8(in, vt);
-  uint16_t* vslot = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * 128 * a.N;
+    for (int j = 0; j < 8; ++j)
+      in[j] = __builtin_nontemporal_load((const u32x4*)(vin + (int64_t)(g * 8 + j) * a.v_ld + c * 8));
+    u32x4 vt[8];
+    transpose8x8(in, vt);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *(u32x4*)(vslot + (int64_t)(c * 8 + i) * a.N + n0) = vt[i];
+    for (int i = 0; i < 8; ++i) *(u32x4*)&tile[c * 8 + i][g * 8] = vt[i];
+  }
+  __syncthreads();
+  uint16_t* vout = a.v_ring + (int64_t)slot * a.slot_elems + ((int64_t)h * 128 + dh * 64) * N + t0;
+  for (uint32_t q = threadIdx.x; q < 64 * ng; q += 256) {  // (dim row, group)
+    const uint32_t r = q / ng, g = q - r * ng;
+    *(u32x4*)(vout + (int64_t)r * N + g * 8) = *(const u32x4*)&tile[r][g * 8];
+  }
 }
 
-// Tokens per launch so that a launch's chunk indices stay below 2^31.
-static uint32_t tokens_per_launch(int H) { return (uint32_t)(((uint32_t)1 << 31) / ((uint32_t)H * 16u)) - 64u; }
+// Tokens per launch: keeps the (token, head group) row index, token * groups,
+// below 2^30.
+uint32_t tokens_per_launch(int H) { return (1u << 30) / (uint32_t)((H + kRopeHpt - 1) / kRopeHpt); }
 
 hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s) {
-  const uint32_t step = tokens_per_launch(a.H);
-  for (uint32_t t = 0; t < (uint32_t)a.n_tokens; t += step) {
-    const uint32_t n = min(step, (uint32_t)a.n_tokens - t);
-    const uint64_t chunks = (uint64_t)n * (uint64_t)a.H * 16u;
-    dim3 grid((unsigned)((chunks + kRopeThreads * kRopeU - 1) / (kRopeThreads * kRopeU)));
+  const uint32_t per_launch = tokens_per_launch(a.H);
+  for (uint32_t t = 0; t < (uint32_t)a.n_tokens; t += per_launch) {
+    const uint32_t n = min(per_launch, (uint32_t)a.n_tokens - t);
+    const uint64_t rows = (uint64_t)n * (uint64_t)((a.H + kRopeHpt - 1) / kRopeHpt);
+    dim3 grid((unsigned)((rows + kRopeRows - 1) / kRopeRows));
     hipLaunchKernelGGL(rope3d_kernel, grid, dim3(kRopeThreads), 0, s, a, t, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -197,16 +207,14 @@ hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s) {
 
 hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
   const uint32_t tokens = (uint32_t)a.n_frames * (uint32_t)a.N;
-  const uint32_t step = tokens_per_launch(a.H);
-  const uint32_t groups = (uint32_t)a.N / 8u;
-  const uint32_t vb_per_fh = (((groups + 7) / 8) * 128 + 255) / 256;
-  const uint32_t v_blocks = (uint32_t)a.n_frames * (uint32_t)a.H * vb_per_fh;  // n_frames*H <= 65535
-  for (uint32_t t = 0; t < tokens; t += step) {
-    const uint32_t n = min(step, tokens - t);
-    const uint64_t k_chunks = (uint64_t)n * a.H * 16u;
-    const uint32_t k_blocks = (uint32_t)((k_chunks + 256u * kRopeU - 1) / (256u * kRopeU));
-    const uint32_t grid = k_blocks + (t == 0 ? v_blocks : 0u);  // value blocks ride with the first piece
-    hipLaunchKernelGGL(roll_kernel, dim3(grid), dim3(256), 0, s, a, k_blocks, t, n);
+  const uint32_t v_blocks = (uint32_t)a.n_frames * (uint32_t)a.H * 2u * (((uint32_t)a.N + kVBlock - 1) / kVBlock);
+  const uint32_t per_launch = tokens_per_launch(a.H);
+  for (uint32_t t = 0; t < tokens; t += per_launch) {
+    const uint32_t n = min(per_launch, tokens - t);
+    const uint64_t rows = (uint64_t)n * (uint64_t)((a.H + kRopeHpt - 1) / kRopeHpt);
+    const uint32_t k_blocks = (uint32_t)((rows + kRopeRows - 1) / kRopeRows);
+    const uint32_t vb = t == 0 ? v_blocks : 0u;  // value blocks ride with the first piece
+    hipLaunchKernelGGL(roll_kernel, dim3(vb + k_blocks), dim3(256), 0, s, a, vb, t, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
