@@ -16,9 +16,11 @@ Trainium" and its digests):
 * ``ring``      -- the rolling frame-window KV cache as a model of frames/slots.
 * ``attention`` -- non-causal softmax attention of query tokens over the
                    window's context frames, float64.
+* ``qkv``       -- the layer's QKV projection and what it leaves in the cache
+                   (q, rotated k, v as bf16), float64.
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/`` against
 closed forms, invariants, library routines or brute force.
 """
 
-from . import bf16, rope3d, ring, attention  # noqa: F401
+from . import bf16, rope3d, ring, attention, qkv  # noqa: F401
