@@ -229,6 +229,39 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c,
                               const rf_attn_segment* segs, int32_t n_segs, float scale,
                               void* stream);
 
+/*
+ * rf_qkv_project -- the layer's QKV projection, fused with the cache write:
+ * for the layer input of frames t0..t0+n_frames-1,
+ *   y = x W^T,  q = y[:, 0:C],  k = y[:, C:2C],  v = y[:, 2C:3C]   (C = H*D),
+ * with q written token-major to `q` (un-rotated: rf_window_attention rotates
+ * queries itself) and k, v rounded to bf16 and written into the ring exactly
+ * as rf_kvcache_roll would write them (k rotated by the bit-exact 3D-RoPE,
+ * v transposed), so k and v never reach memory as tensors of their own.  The
+ * ring bookkeeping (overwrite in place, append, evict the oldest) and the
+ * descriptor update are those of rf_kvcache_roll.
+ *
+ * Source: every layer reads and writes a rolling KV cache and rotates its
+ * queries and keys over time, height and width ("Amazon and Reactor tune
+ * Trainium for real-time video generation", section "Three problems for
+ * generic compilers"), with 12 attention heads (ai4snews digest, second
+ * paragraph).  The projection is not printed on the pages; this is the
+ * standard multi-head self-attention projection (one [3C][C] weight: the q
+ * rows, then the k rows, then the v rows; feature h*D + d of each block is
+ * dimension d of head h).
+ *
+ * x: token-major [n_frames*N][x_ld] bf16 layer input, x_ld >= C.
+ * w: [3C][w_ld] bf16 weight (row = output feature, w_ld >= C).
+ * q: token-major [n_frames*N][q_ld] bf16 output, q_ld >= C; must not overlap
+ *    x, w or the ring.
+ * All three 16-byte aligned, ld multiples of 8 and at most 2^22.
+ * Precision: bf16 products accumulated in float32 over the C input
+ * features, rounded once to bf16 (round to nearest even).
+ * Requirements and errors on the ring, t0 and n_frames as rf_kvcache_roll.
+ */
+rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_t x_ld,
+                         const void* w, int64_t w_ld, void* q, int64_t q_ld, int64_t t0,
+                         int32_t n_frames, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,7 @@ first call raises.
     ctx = Context()                                   # 30x52 grid, 12 heads of 128
     cache = KVCache(ctx, capacity=21)                 # ring of 21 frame slots
     cache.roll(k_new, v_new, t0)                      # RoPE(K) + V^T into the ring
+    cache.project(x, w, q, t0)                        # or: q = x Wq^T, k and v straight into the ring
     window_attention(ctx, cache, [Segment(q, q_t0, o, ctx_t0, ctx_frames), ...])
 """
 
@@ -28,7 +29,7 @@ MAX_SEGMENTS = 8
 
 # Every entry point include/rfattn.h declares.
 EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
-           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention")
+           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention", "rf_qkv_project")
 
 
 class RfError(RuntimeError):
@@ -85,6 +86,8 @@ def lib():
         L.rf_window_attention.argtypes = [vp, ctypes.POINTER(KVCacheDesc),
                                           ctypes.POINTER(SegmentDesc), i32, ctypes.c_float, vp]
         L.rf_window_attention.restype = i32
+        L.rf_qkv_project.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, vp, i64, i64, i32, vp]
+        L.rf_qkv_project.restype = i32
         _lib = L
     return _lib
 
@@ -195,6 +198,22 @@ class KVCache:
         n = nk // c.tokens_per_frame
         _check(lib().rf_kvcache_roll(c.handle, ctypes.byref(self.desc), kp, kld, vp, vld, t0, n,
                                      _stream(stream)))
+
+    def project(self, x, w, q, t0, stream=None):
+        """QKV projection of the layer input x ([n*N, H*D]) with weight w ([3*H*D, H*D]):
+        queries into q ([n*N, H, D] or [n*N, H*D]); rotated keys and transposed values
+        of frames t0.. into the ring, as roll() would write them."""
+        c = self.ctx
+        xp, xld, nx = _token_major(x, "x", c.n_heads, c.head_dim)
+        qp, qld, nq = _token_major(q, "q", c.n_heads, c.head_dim)
+        wp, wld, nw = _token_major(w, "w", c.n_heads, c.head_dim)
+        if nw != 3 * c.n_heads * c.head_dim:
+            raise ValueError("w must be [3*H*D, H*D]")
+        if nx != nq or nx % c.tokens_per_frame:
+            raise ValueError("x and q must hold the same whole number of frames")
+        n = nx // c.tokens_per_frame
+        _check(lib().rf_qkv_project(c.handle, ctypes.byref(self.desc), xp, xld, wp, wld, qp, qld, t0, n,
+                                    _stream(stream)))
 
     def plan_roll(self, t0, n_frames):
         """(first, count) the ring would have after rolling frames t0..t0+n_frames-1."""

@@ -42,7 +42,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librfattn.so")
-PLAIN_SOURCES = ["api.hip", "rope_roll.hip"]
+PLAIN_SOURCES = ["api.hip", "rope_roll.hip", "qkv_proj.hip"]
 ATTN_SOURCE = "window_attn.hip"
 ATTN_KERNEL_PREFIX = "_ZN6rfattn18window_attn_kernel"
 ATTN_AGPRS = 96        # a[0:63]: O^T accumulators; 32 more: the Q' fragments

@@ -47,6 +47,7 @@ rf_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxTokens = int64_t(1) << 24;  // device index math is exact below this
+constexpr int64_t kMaxProjLd = int64_t(1) << 22;  // 256 rows of the projection's operands: < 2^31 bytes
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -163,6 +164,7 @@ rf_status rf_create(const rf_geom* g, rf_ctx** out) {
   e = hipMalloc((void**)&part, (size_t)2 * max_workers * kPartFloats * sizeof(float));
   if (e == hipSuccess) e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = prepare_window_attn();
+  if (e == hipSuccess) e = prepare_qkv_proj();
   if (e != hipSuccess) {
     (void)hipFree(d);
     if (part) (void)hipFree(part);
@@ -288,6 +290,58 @@ rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, i
   a.tab = ctx->tab;
   hipError_t e = launch_roll(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kvcache roll launch");
+  c->first = after.first;
+  c->count = after.count;
+  return RF_OK;
+}
+
+rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_t x_ld, const void* w,
+                         int64_t w_ld, void* q, int64_t q_ld, int64_t t0, int32_t n_frames, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if ((st = check_ring(c, true)) != RF_OK) return st;
+  const rf_geom& g = ctx->g;
+  const int64_t C = (int64_t)g.n_heads * g.head_dim;
+  if ((st = check_tensor(x, x_ld, C, "x")) != RF_OK) return st;
+  if ((st = check_tensor(w, w_ld, C, "w")) != RF_OK) return st;
+  if ((st = check_tensor(q, q_ld, C, "q")) != RF_OK) return st;
+  if (x_ld > kMaxProjLd || w_ld > kMaxProjLd || q_ld > kMaxProjLd)
+    return fail(RF_ERR_SHAPE, "row strides must be at most 2^22 elements");
+  rf_kvcache after;
+  if ((st = rf_kvcache_plan_roll(c, t0, n_frames, &after)) != RF_OK) return st;
+  if (t0 < 0 || t0 + n_frames > g.max_frame)
+    return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
+                (long long)(t0 + n_frames - 1), (long long)g.max_frame);
+  const int64_t N = (int64_t)g.grid_h * g.grid_w;
+  const int64_t M = (int64_t)n_frames * N;
+  if (M >= kMaxTokens) return fail(RF_ERR_SHAPE, "too many tokens in one projection");
+
+  ProjArgs a;
+  a.x = (const uint16_t*)x;
+  a.w = (const uint16_t*)w;
+  a.q = (uint16_t*)q;
+  a.k_ring = (uint16_t*)c->k;
+  a.v_ring = (uint16_t*)c->v;
+  a.x_ld = x_ld;
+  a.w_ld = w_ld;
+  a.q_ld = q_ld;
+  a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;
+  a.t0 = t0;
+  a.M = (int)M;
+  a.C = (int)C;
+  a.N = (int)N;
+  a.gw = g.grid_w;
+  a.W = c->capacity;
+  a.slot0 = (int)mod(t0, c->capacity);
+  a.tiles_per_part = (int)((C + 255) / 256);
+  a.f_tiles = 3 * a.tiles_per_part;
+  a.n_tiles = (int)((M + 255) / 256) * a.f_tiles;
+  a.inv_n = 1.0f / (float)N;
+  a.inv_gw = 1.0f / (float)g.grid_w;
+  a.tab = ctx->tab;
+  hipError_t e = launch_qkv_proj(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
   c->first = after.first;
   c->count = after.count;
   return RF_OK;

@@ -69,9 +69,29 @@ struct AttnArgs {
   RopeTables tab;
 };
 
+// Fused QKV projection: y = x W^T, q token-major, k rotated into K ring slots,
+// v transposed into V ring slots (tiles of 256 tokens x 256 features; each of
+// q, k, v has tiles_per_part = ceil(C / 256) feature tiles).
+struct ProjArgs {
+  const uint16_t* x;     // [M][x_ld], M = n_frames * N tokens of frames t0..
+  const uint16_t* w;     // [3C][w_ld]
+  uint16_t* q;           // [M][q_ld]
+  uint16_t* k_ring;      // [W][H][N][D]
+  uint16_t* v_ring;      // [W][H][D][N]
+  int64_t x_ld, w_ld, q_ld;
+  int64_t slot_elems;    // H*N*D
+  int64_t t0;            // frame of token 0
+  int M, C, N, gw, W, slot0;
+  int n_tiles, f_tiles, tiles_per_part;
+  float inv_n, inv_gw;   // 1/N, 1/gw for the exact small divisions
+  RopeTables tab;
+};
+
 hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s);
 hipError_t launch_roll(const RollArgs& a, hipStream_t s);
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 hipError_t prepare_window_attn();  // once per device, before the first launch
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+hipError_t prepare_qkv_proj();     // once per device, before the first launch
 
 }  // namespace rfattn

@@ -9,7 +9,8 @@ A frame's tensor depends only on (workload id, step, frame index, tensor id),
 never on how frames are batched into calls:
 ``numpy.random.default_rng([cfg, step, t, tensor_id]).standard_normal``.
 Tensor ids: 0 = q, 1 = k, 2 = v of the noisy (denoise-pass) frame; 3, 4, 5 the
-same of the clean frame that the cache-update pass writes.
+same of the clean frame that the cache-update pass writes; 6 the layer input x
+that the QKV projection maps to q, k, v (its weight comes from ``qkv_weight``).
 """
 
 from dataclasses import dataclass
@@ -55,6 +56,25 @@ def frame(geom, cfg, step, t, tensor_id):
     rng = np.random.default_rng([int(cfg), int(step), int(t), int(tensor_id)])
     shape = (geom.tokens_per_frame, geom.n_heads, geom.head_dim)
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+# Tensor id of a frame's layer input x (the QKV projection's input), [N, H*D].
+LAYER_IN = 6
+
+
+def layer_input(geom, cfg, step, t0, n):
+    """Frames t0..t0+n-1 of the layer input: bf16 bits [n*N, H*D] drawn from N(0, 1)."""
+    x = frames(geom, cfg, step, t0, n, LAYER_IN)
+    return x.reshape(x.shape[0], geom.n_heads * geom.head_dim)
+
+
+def qkv_weight(geom, cfg):
+    """A projection weight [3C, C] (C = H*D): bf16 bits drawn from N(0, 1/C), so that
+    projections of N(0, 1) inputs are again about N(0, 1)."""
+    c = geom.n_heads * geom.head_dim
+    rng = np.random.default_rng([int(cfg), 1 << 20, 3, c])
+    w = rng.standard_normal((3 * c, c), dtype=np.float32) * np.float32(1.0 / np.sqrt(c))
+    return f32_to_bf16_bits(w)
 
 
 def frames(geom, cfg, step, t0, n, tensor_id):

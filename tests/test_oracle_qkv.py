@@ -95,11 +95,17 @@ def test_rounding_is_once_from_float64():
 def test_float32_accumulation_is_within_one_bf16_step(seed):
     """The tolerance the device parity test uses: a float32 running sum over the 1,536
     input features, rounded to bf16, equals the float64-then-bf16 value except where
-    the two straddle a rounding boundary, and then it is one bf16 step away."""
+    the two straddle a rounding boundary, and then it is within one bf16 step plus the
+    worst-case float32 summation error E = (C - 1) 2^-24 sum |x_c w_c| (which matters
+    for outputs near zero).  Two weight rows are built to cancel almost exactly."""
     rng = np.random.default_rng(seed)
     C, L, F = 1536, 16, 64
     xb = _bits(rng.standard_normal((L, C)))
-    wb = _bits(rng.standard_normal((F, C)) / np.sqrt(C))
+    w0 = rng.standard_normal((F, C)) / np.sqrt(C)
+    x0 = bf16.bits_to_f64(xb)
+    for r in (0, 1):  # make x[r] . w[r] tiny: remove its projection on x[r]
+        w0[r] -= (w0[r] @ x0[r]) / (x0[r] @ x0[r]) * x0[r]
+    wb = _bits(w0)
     x, w = bf16.bits_to_f64(xb), bf16.bits_to_f64(wb)
     exact = x @ w.T
     acc = np.zeros((L, F), dtype=np.float32)
@@ -109,6 +115,9 @@ def test_float32_accumulation_is_within_one_bf16_step(seed):
     ref = bf16.f64_to_bits(exact)
     same = dev == ref
     assert same.mean() > 0.98
-    step = np.abs(bf16.bits_to_f64(dev) - bf16.bits_to_f64(ref))
-    ulp = np.abs(bf16.round_f64(exact)) * 2.0 ** -7
-    assert np.all(step[~same] <= ulp[~same] * 1.0001)
+    diff = np.abs(bf16.bits_to_f64(dev) - bf16.bits_to_f64(ref))
+    E = (C - 1) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+    assert np.all(diff <= np.abs(bf16.bits_to_f64(ref)) * 2.0 ** -7 * 1.01 + 1.02 * E)
+    # away from zero the difference is at most one bf16 step
+    big = np.abs(exact) > 64 * E
+    assert np.all(diff[big] <= np.abs(bf16.round_f64(exact[big])) * 2.0 ** -7 * 1.0001)
