@@ -258,7 +258,7 @@ def main():
     # ---- extras (not part of the timed steps): denoise-only launch, the cache-update
     # pass alone, standalone RoPE, cold/warm single calls, the 30-step dynamic fill ----
     denoise_ms = rope_ms = update_ms = None
-    dynamic = None
+    dynamic = projection = None
     cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
@@ -289,6 +289,7 @@ def main():
         torch.cuda.synchronize()
         update_ms = e0.elapsed_time(e1) / reps
         dynamic = dynamic_fill(rf, ctx, W, N, H, D, pool, stream)
+        projection = qkv_projection(rf, synth, g, ctx, W, stream)
 
         # cold (a 1 GiB fill evicts L2 and the 256 MB MALL before each rep) and warm
         # single-call times of the standalone RoPE and of the step's roll; the roll
@@ -386,6 +387,8 @@ def main():
             "frac_bf16_peak": round(flops_update / (update_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if dynamic is not None:
         out["dynamic_30_steps"] = dynamic
+    if projection is not None:
+        out["qkv_projection_16"] = projection
 
     if not args.no_cpu_baseline:
         ctx_frames = [written[t] for t in range(last_s - 6, last_s + 15)]
@@ -430,6 +433,49 @@ def dynamic_fill(rf, ctx, W, N, H, D, pool, stream):
            "ms_total": round(ms, 3), "ms_per_step": round(ms / 30, 4),
            "TFLOP": round(flops / 1e12, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2)}
     return res
+
+
+def qkv_projection(rf, synth, g, ctx, W, stream, reps=10):
+    """rf_qkv_project of the step's 16 frames (24,960 tokens x 1,536 -> 4,608 features):
+    q token-major, rotated keys and transposed values into a 21-frame ring.  Synthetic
+    layer input and N(0, 1/C) weights.  For context, the time of torch's library GEMM of
+    the same shape alone (no epilogue, no cache write) is reported next to it."""
+    import torch
+
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    C = H * D
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = up(synth.layer_input(g, 14, 0, 0, 16))
+    w = up(synth.qkv_weight(g, 14))
+    q = torch.empty((16 * N, H, D), dtype=torch.bfloat16, device=dev)
+    cache = rf.KVCache(ctx, W)
+    cache.project(x, w, q, 0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cache.project(x, w, q, 0)  # rewrites frames 0..15 in place
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    y = x @ w.t()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        y = x @ w.t()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib_ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * 16 * N * 3 * C * C
+    del y, cache
+    return {"tokens": 16 * N, "in_features": C, "out_features": 3 * C, "ms": round(ms, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "library_gemm_only_ms": round(lib_ms, 4)}
 
 
 def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):

@@ -337,6 +337,7 @@ rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_
   a.tiles_per_part = (int)((C + 255) / 256);
   a.f_tiles = 3 * a.tiles_per_part;
   a.n_tiles = (int)((M + 255) / 256) * a.f_tiles;
+  a.n_workers = std::max(8, ctx->max_workers / kWorkersPerCu / 8 * 8);
   a.inv_n = 1.0f / (float)N;
   a.inv_gw = 1.0f / (float)g.grid_w;
   a.tab = ctx->tab;

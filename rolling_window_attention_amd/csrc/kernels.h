@@ -83,6 +83,7 @@ struct ProjArgs {
   int64_t t0;            // frame of token 0
   int M, C, N, gw, W, slot0;
   int n_tiles, f_tiles, tiles_per_part;
+  int n_workers;         // persistent work-groups: one per CU, a multiple of 8
   float inv_n, inv_gw;   // 1/N, 1/gw for the exact small divisions
   RopeTables tab;
 };

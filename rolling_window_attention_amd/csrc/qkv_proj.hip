@@ -32,6 +32,13 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef RF_QKV_WAVES
+#define RF_QKV_WAVES 8
+#endif
+#ifndef RF_QKV_PREFETCH
+#define RF_QKV_PREFETCH 1
+#endif
+
 namespace rfattn {
 
 namespace {
@@ -42,8 +49,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kWaves = RF_QKV_WAVES;     // 4 (one per SIMD) or 8 (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;               // tokens and features per tile
+constexpr int kBW = kTile / (kWaves / 2);  // B-side columns per wave: 128 or 64
+constexpr int kNB = kBW / 32;            // B-side 32-blocks per wave
+constexpr int kSRows = kThreads / 8;     // operand rows staged per pass (8 chunks of 16 B a row)
+constexpr int kSPass = kTile / kSRows;   // staging passes per operand tile
 constexpr int kStepK = 64;               // reduction per staged step
 constexpr int kSRow = kStepK + 8;        // LDS row stride of a staged operand (144 B)
 constexpr int kSTile = kTile * kSRow;    // elements of one staged operand tile
@@ -58,6 +70,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+#ifndef RF_QKV_NT
+#define RF_QKV_NT 1
+#endif
+// Output stores: non-temporal (the outputs are not read again by this kernel).
+__device__ __forceinline__ void out_store(u32x4* p, u32x4 v) {
+  if (RF_QKV_NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 // Work-group id -> tile index, each XCD walking a contiguous run (a bijection).
 __device__ __forceinline__ int xcd_tile(int bid, int total) {
   const int per = (total + kXcds - 1) / kXcds;
@@ -69,91 +92,116 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+// A tile's coordinates and operand buffers.
+struct TileRef {
+  int part;      // 0: q, 1: k, 2: v (uniform)
+  int fl0;       // first feature inside the part
+  int m0;        // first token
+  int rows_x;    // valid tokens
+  int rows_w;    // valid features
+  __amdgpu_buffer_rsrc_t xrs, wrs;  // rows past the valid ones read 0
+};
+
+__device__ __forceinline__ TileRef tile_ref(const ProjArgs& a, int tile) {
+  TileRef t;
+  const int mt = tile / a.f_tiles;
+  const int ft = tile - mt * a.f_tiles;
+  t.part = ft / a.tiles_per_part;
+  t.fl0 = (ft - t.part * a.tiles_per_part) * kTile;
+  t.m0 = mt * kTile;
+  t.rows_x = min(kTile, a.M - t.m0);
+  t.rows_w = min(kTile, a.C - t.fl0);
+  t.xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x + (int64_t)t.m0 * a.x_ld), 0,
+                                            (int)((uint32_t)t.rows_x * (uint32_t)a.x_ld * 2u), kBufferWord3);
+  t.wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w + ((int64_t)t.part * a.C + t.fl0) * a.w_ld),
+                                            0, (int)((uint32_t)t.rows_w * (uint32_t)a.w_ld * 2u), kBufferWord3);
+  return t;
+}
+
+// Step kt's operand rows of tile t into registers: thread -> rows (tid >> 3) +
+// kSRows i, 16-byte chunk tid & 7 of the step's 64 k.  The whole offset goes in
+// the vector operand: the buffer's range check (which turns rows past the valid
+// ones into zeros) does not include the scalar offset.
+__device__ __forceinline__ void load_step(const ProjArgs& a, const TileRef& t, int kt, u32x4 (&xs)[kSPass],
+                                          u32x4 (&ws)[kSPass]) {
+  const int srow = threadIdx.x >> 3, schunk = threadIdx.x & 7;
+  const uint32_t x_lane = (uint32_t)srow * (uint32_t)a.x_ld * 2u + 16u * schunk + (uint32_t)kt * 128u;
+  const uint32_t w_lane = (uint32_t)srow * (uint32_t)a.w_ld * 2u + 16u * schunk + (uint32_t)kt * 128u;
+  const uint32_t x_rows = (uint32_t)kSRows * (uint32_t)a.x_ld * 2u, w_rows = (uint32_t)kSRows * (uint32_t)a.w_ld * 2u;
+#pragma unroll
+  for (int i = 0; i < kSPass; ++i) {
+    xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t.xrs, x_lane + (uint32_t)i * x_rows, 0, 0));
+    ws[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t.wrs, w_lane + (uint32_t)i * w_rows, 0, 0));
+  }
+}
+
+// One 256 x 256 output tile whose first step is already in xs/ws: main loop, then
+// (with the next tile's first step put in flight in xs/ws, if there is one) the
+// epilogue through LDS.
+__device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, const TileRef& t, bool has_next,
+                                          const TileRef& next, u32x4 (&xs)[kSPass], u32x4 (&ws)[kSPass]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lr = lane & 31;
   const int hf = lane >> 5;
-  const int wa = wave & 1, wb = wave >> 1;  // wave's 128-row block of the A and B sides
-
-  const int tile = xcd_tile(blockIdx.x, a.n_tiles);
-  const int mt = tile / a.f_tiles;
-  const int ft = tile - mt * a.f_tiles;
-  const int part = ft / a.tiles_per_part;   // 0: q, 1: k, 2: v (wave-uniform)
-  const int fl0 = (ft - part * a.tiles_per_part) * kTile;  // first feature inside the part
-  const int m0 = mt * kTile;
-  const int rows_x = min(kTile, a.M - m0);   // valid tokens of the tile
-  const int rows_w = min(kTile, a.C - fl0);  // valid features of the tile
+  const int wa = wave & 1, wb = wave >> 1;  // wave's 128-row A block and kBW-column B block
+  const int part = t.part, fl0 = t.fl0, m0 = t.m0, rows_x = t.rows_x, rows_w = t.rows_w;
   const bool is_v = part == 2;
-
-  // operand tiles through raw buffer loads: rows past the valid ones read 0
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.x + (int64_t)m0 * a.x_ld), 0, (int)((uint32_t)rows_x * (uint32_t)a.x_ld * 2u),
-      kBufferWord3);
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.w + ((int64_t)part * a.C + fl0) * a.w_ld), 0,
-      (int)((uint32_t)rows_w * (uint32_t)a.w_ld * 2u), kBufferWord3);
-  // thread -> rows (tid >> 3) + 32 i, 16-byte chunk tid & 7 of the step's 64 k
   const int srow = tid >> 3, schunk = tid & 7;
-  const uint32_t x_lane = (uint32_t)srow * (uint32_t)a.x_ld * 2u + 16u * schunk;
-  const uint32_t w_lane = (uint32_t)srow * (uint32_t)a.w_ld * 2u + 16u * schunk;
-  const uint32_t x_row32 = 32u * (uint32_t)a.x_ld * 2u, w_row32 = 32u * (uint32_t)a.w_ld * 2u;
-  u32x4 xs[8], ws[8];
-  // The whole offset goes in the vector operand: the buffer's range check (which
-  // turns rows past the valid ones into zeros) does not include the scalar offset.
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xrs, x_lane + (uint32_t)i * x_row32 + (uint32_t)kt * 128u, 0, 0));
-      ws[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            wrs, w_lane + (uint32_t)i * w_row32 + (uint32_t)kt * 128u, 0, 0));
-    }
-  };
   auto stage = [&](int buf) {
     uint16_t* X = lds + buf * 2 * kSTile;
     uint16_t* Wt = X + kSTile;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *(u32x4*)(X + (srow + 32 * i) * kSRow + 8 * schunk) = xs[i];
-      *(u32x4*)(Wt + (srow + 32 * i) * kSRow + 8 * schunk) = ws[i];
+    for (int i = 0; i < kSPass; ++i) {
+      *(u32x4*)(X + (srow + kSRows * i) * kSRow + 8 * schunk) = xs[i];
+      *(u32x4*)(Wt + (srow + kSRows * i) * kSRow + 8 * schunk) = ws[i];
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kNB];
 #pragma unroll
   for (int ia = 0; ia < 4; ++ia)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) acc[ia][ib] = f32x16{};
+    for (int ib = 0; ib < kNB; ++ib) acc[ia][ib] = f32x16{};
 
   const int nk = a.C / kStepK;
-  load(0);
   stage(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
+    if (kt + 1 < nk) load_step(a, t, kt + 1, xs, ws);
     const uint16_t* X = lds + (kt & 1) * 2 * kSTile;
     const uint16_t* At = is_v ? X : X + kSTile;
     const uint16_t* Bt = is_v ? X + kSTile : X;
+    bf16x8 af[2][4], bfr[2][kNB];
+    auto frags = [&](int set, int s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[set][i] = *(const bf16x8*)(At + (128 * wa + 32 * i + lr) * kSRow + 16 * s + 8 * hf);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        bfr[set][i] = *(const bf16x8*)(Bt + (kBW * wb + 32 * i + lr) * kSRow + 16 * s + 8 * hf);
+    };
+    if (RF_QKV_PREFETCH) frags(0, 0);
 #pragma unroll
     for (int s = 0; s < kStepK / 16; ++s) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *(const bf16x8*)(At + (128 * wa + 32 * i + lr) * kSRow + 16 * s + 8 * hf);
-        bfr[i] = *(const bf16x8*)(Bt + (128 * wb + 32 * i + lr) * kSRow + 16 * s + 8 * hf);
+      const int set = RF_QKV_PREFETCH ? (s & 1) : 0;
+      if (RF_QKV_PREFETCH) {
+        if (s + 1 < kStepK / 16) frags(set ^ 1, s + 1);  // next substep's fragments in flight
+      } else {
+        frags(0, s);
       }
 #pragma unroll
       for (int ia = 0; ia < 4; ++ia)
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-          acc[ia][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ia], bfr[ib], acc[ia][ib], 0, 0, 0);
+        for (int ib = 0; ib < kNB; ++ib)
+          acc[ia][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][ia], bfr[set][ib], acc[ia][ib], 0, 0, 0);
     }
     if (kt + 1 < nk) stage((kt + 1) & 1);
     __syncthreads();
   }
+
+  if (has_next) load_step(a, next, 0, xs, ws);  // in flight during the epilogue
 
   // ---- epilogue: bf16 image [B-side row][A-side column] in LDS ---------------------
   // Accumulator register 4 g + j of block (ia, ib) holds A-side row
@@ -162,38 +210,45 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjArgs a) {
 #pragma unroll
   for (int ia = 0; ia < 4; ++ia)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < kNB; ++ib)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
         w[0] = pack2(acc[ia][ib][4 * g + 0], acc[ia][ib][4 * g + 1]);
         w[1] = pack2(acc[ia][ib][4 * g + 2], acc[ia][ib][4 * g + 3]);
-        *(u32x2*)(T + (128 * wb + 32 * ib + lr) * kORow + 128 * wa + 32 * ia + 8 * g + 4 * hf) = w;
+        *(u32x2*)(T + (kBW * wb + 32 * ib + lr) * kORow + 128 * wa + 32 * ia + 8 * g + 4 * hf) = w;
       }
   __syncthreads();
 
   const int N = a.N;
   const int64_t head_elems = (int64_t)N * kHeadDim;
-  if (!is_v) {
+  if (part == 0) {
     // token rows: 32 chunks of 8 features each
     for (int idx = tid; idx < kTile * 32; idx += kThreads) {
       const int ml = idx >> 5, c = idx & 31;
       if (ml >= rows_x || 8 * c >= rows_w) continue;
-      const u32x4 v = *(const u32x4*)(T + ml * kORow + 8 * c);
+      out_store((u32x4*)(a.q + (int64_t)(m0 + ml) * a.q_ld + fl0 + 8 * c), *(const u32x4*)(T + ml * kORow + 8 * c));
+    }
+  } else if (part == 1) {
+    // token rows: a thread takes chunk column cc (pairs 4cc..4cc+3) of one token in
+    // both heads of the tile, sharing the pairs' cos/sin
+    for (int idx = tid; idx < kTile * 16; idx += kThreads) {
+      const int ml = idx >> 4, cc = idx & 15;
+      if (ml >= rows_x) continue;
       const int mg = m0 + ml;
-      const int f = fl0 + 8 * c;  // feature inside the part
-      if (part == 0) {
-        *(u32x4*)(a.q + (int64_t)mg * a.q_ld + f) = v;
-      } else {
-        uint32_t pin, col;
-        const uint32_t fr = small_div((uint32_t)mg, (uint32_t)N, a.inv_n, &pin);
-        const uint32_t row = small_div(pin, (uint32_t)a.gw, a.inv_gw, &col);
-        int slot = a.slot0 + (int)fr;
-        if (slot >= a.W) slot -= a.W;  // slot0 < W and fr < W
-        const int h = f / kHeadDim, d = f - h * kHeadDim;
-        const ChunkCS cs = rope_chunk_cs_of(a.tab, d / 2, a.t0 + fr, (int)row, (int)col);
-        *(u32x4*)(a.k_ring + (int64_t)slot * a.slot_elems + h * head_elems + (int64_t)pin * kHeadDim + d) =
-            rope_chunk_cs(v, cs);
+      uint32_t pin, col;
+      const uint32_t fr = small_div((uint32_t)mg, (uint32_t)N, a.inv_n, &pin);
+      const uint32_t row = small_div(pin, (uint32_t)a.gw, a.inv_gw, &col);
+      int slot = a.slot0 + (int)fr;
+      if (slot >= a.W) slot -= a.W;  // slot0 < W and fr < W
+      const ChunkCS cs = rope_chunk_cs_of(a.tab, 4 * cc, a.t0 + fr, (int)row, (int)col);
+      uint16_t* kdst = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)pin * kHeadDim + 8 * cc;
+#pragma unroll
+      for (int hh = 0; hh < kTile / kHeadDim; ++hh) {
+        const int f = fl0 + hh * kHeadDim;  // first feature of the head inside the part
+        if (hh * kHeadDim >= rows_w) break;
+        const u32x4 v = *(const u32x4*)(T + ml * kORow + hh * kHeadDim + 8 * cc);
+        out_store((u32x4*)(kdst + (f / kHeadDim) * head_elems), rope_chunk_cs(v, cs));
       }
     }
   } else {
@@ -208,8 +263,30 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjArgs a) {
       if (slot >= a.W) slot -= a.W;
       const int f = fl0 + fl;
       const int h = f / kHeadDim, d = f - h * kHeadDim;
-      *(u32x4*)(a.v_ring + (int64_t)slot * a.slot_elems + h * head_elems + (int64_t)d * N + n0) = v;
+      out_store((u32x4*)(a.v_ring + (int64_t)slot * a.slot_elems + h * head_elems + (int64_t)d * N + n0), v);
     }
+  }
+}
+
+// Persistent: one work-group per CU walks tiles i = blockIdx.x, + gridDim.x, ...;
+// a tile's stores drain while the next tile computes.  Tile i goes to XCD i % 8
+// with the grid a multiple of 8, and xcd_tile gives each XCD a contiguous run.
+__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  int i = blockIdx.x;
+  if (i >= a.n_tiles) return;
+  u32x4 xs[kSPass], ws[kSPass];
+  TileRef cur = tile_ref(a, xcd_tile(i, a.n_tiles));
+  load_step(a, cur, 0, xs, ws);
+  for (;;) {
+    const int nxt = i + (int)gridDim.x;
+    const bool has_next = nxt < a.n_tiles;
+    const TileRef next = tile_ref(a, xcd_tile(has_next ? nxt : i, a.n_tiles));
+    proj_tile(a, lds, cur, has_next, next, xs, ws);
+    if (!has_next) break;
+    __syncthreads();  // the LDS image is read out before the next tile stages into it
+    i = nxt;
+    cur = next;
   }
 }
 
@@ -220,7 +297,8 @@ hipError_t prepare_qkv_proj() {
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   if (a.n_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)a.n_tiles), dim3(kThreads), kLds, s, a);
+  const int grid = min(a.n_tiles, a.n_workers);
+  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)grid), dim3(kThreads), kLds, s, a);
   return hipGetLastError();
 }
 
