@@ -29,14 +29,16 @@
 // rotated on the way, with the roll's arithmetic), feature rows of 256 tokens
 // for v.  Tiles are numbered so that each XCD walks consecutive feature tiles
 // of one token tile (x rows reused from L2).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 #ifndef RF_QKV_WAVES
 #define RF_QKV_WAVES 8
 #endif
-#ifndef RF_QKV_PREFETCH
-#define RF_QKV_PREFETCH 1
+#ifndef RF_QKV_SGB
+#define RF_QKV_SGB 1
 #endif
 
 namespace rfattn {
@@ -168,8 +170,19 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
   const int nk = a.C / kStepK;
   stage(0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_step(a, t, kt + 1, xs, ws);
+  // One reduction step on LDS buffer kt & 1; with `more`, the next step's global
+  // loads are issued during the first substep's MFMAs and staged into the other
+  // buffer during the last one.  Each substep's MFMAs run while the next
+  // substep's fragments are read.  With RF_QKV_SGB the interleave is fixed with
+  // scheduling groups: one fragment read, global load or staging write after
+  // each MFMA.
+  auto kstep = [&](int kt, auto more) {
+    constexpr bool kMore = decltype(more)::value;
+    constexpr int kSub = kStepK / 16;
+    constexpr int kMf = 4 * kNB;        // MFMAs per substep
+    constexpr int kRd = 4 + kNB;        // fragment reads per substep
+    constexpr int kVm = 2 * kSPass;     // global loads (and staging writes) per step
+    if constexpr (kMore) load_step(a, t, kt + 1, xs, ws);
     const uint16_t* X = lds + (kt & 1) * 2 * kSTile;
     const uint16_t* At = is_v ? X : X + kSTile;
     const uint16_t* Bt = is_v ? X + kSTile : X;
@@ -182,24 +195,38 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
       for (int i = 0; i < kNB; ++i)
         bfr[set][i] = *(const bf16x8*)(Bt + (kBW * wb + 32 * i + lr) * kSRow + 16 * s + 8 * hf);
     };
-    if (RF_QKV_PREFETCH) frags(0, 0);
+    frags(0, 0);
 #pragma unroll
-    for (int s = 0; s < kStepK / 16; ++s) {
-      const int set = RF_QKV_PREFETCH ? (s & 1) : 0;
-      if (RF_QKV_PREFETCH) {
-        if (s + 1 < kStepK / 16) frags(set ^ 1, s + 1);  // next substep's fragments in flight
-      } else {
-        frags(0, s);
-      }
+    for (int s = 0; s < kSub; ++s) {
+      const int set = s & 1;
+      if (s + 1 < kSub) frags(set ^ 1, s + 1);
 #pragma unroll
       for (int ia = 0; ia < 4; ++ia)
 #pragma unroll
         for (int ib = 0; ib < kNB; ++ib)
           acc[ia][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][ia], bfr[set][ib], acc[ia][ib], 0, 0, 0);
     }
-    if (kt + 1 < nk) stage((kt + 1) & 1);
+    if constexpr (kMore) stage((kt + 1) & 1);
+#if RF_QKV_SGB
+    __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);  // substep 0's fragments first
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) {
+#pragma unroll
+      for (int i = 0; i < kMf; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+        if (s + 1 < kSub && i < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        if (kMore && s == 0 && i < kVm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        if (kMore && s == kSub - 1 && i < kVm) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+    }
+#endif
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    kstep(kt, std::true_type{});
     __syncthreads();
   }
+  kstep(nk - 1, std::false_type{});
+  __syncthreads();
 
   if (has_next) load_step(a, next, 0, xs, ws);  // in flight during the epilogue
 
