@@ -230,6 +230,37 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c,
                               void* stream);
 
 /*
+ * rf_set_frame_shift / rf_add_frame_shift -- replaying a captured steady-state
+ * step.  A window step repeats with every frame index one higher than the
+ * step before (the window slides by one frame; "Amazon and Reactor tune
+ * Trainium for real-time video generation", section "Three problems for
+ * generic compilers": frames generated and evicted in a sliding window, every
+ * layer reading and writing its rolling KV cache).  With a shift set, every
+ * later launch on ctx (rf_rope3d_apply, rf_kvcache_roll, rf_window_attention,
+ * rf_qkv_project) reads the int64 at d_shift (device memory) when its kernels
+ * run, clamps it to 0..max_shift, and adds it to all absolute frame indices of
+ * the call: RoPE positions and ring slots (mod capacity).  A caller can thus
+ * capture one step's launches in a HIP graph once (host arguments of step s)
+ * and replay it for steps s+1, s+2, ... by advancing *d_shift inside the graph
+ * with rf_add_frame_shift.
+ *
+ * rf_set_frame_shift: d_shift 8-byte aligned device memory owned by the caller
+ *   (NULL turns the shift off); 0 <= max_shift < max_frame.  From then on the
+ *   host validation of every call checks its frame ranges with max_shift
+ *   added, so no replay within the clamp reads past the RoPE tables.  The
+ *   caller orders this call after any queued work of the context.
+ * rf_add_frame_shift: enqueue *d_shift += delta on `stream` (one-thread
+ *   kernel; capturable).
+ * Replays do not update the host-side rf_kvcache descriptors: advance them
+ * with rf_kvcache_plan_roll if the caller needs them afterwards.  The shift
+ * moves every frame index alike; the ring must hold the frames that the
+ * shifted calls expect, which holds when each replayed step rolls its own new
+ * frames (the usual step: roll, then attention).
+ */
+rf_status rf_set_frame_shift(rf_ctx* ctx, const int64_t* d_shift, int64_t max_shift);
+rf_status rf_add_frame_shift(const rf_ctx* ctx, int64_t* d_shift, int64_t delta, void* stream);
+
+/*
  * rf_qkv_project -- the layer's QKV projection, fused with the cache write:
  * for the layer input of frames t0..t0+n_frames-1,
  *   y = x W^T,  q = y[:, 0:C],  k = y[:, C:2C],  v = y[:, 2C:3C]   (C = H*D),

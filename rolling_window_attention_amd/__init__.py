@@ -29,7 +29,8 @@ MAX_SEGMENTS = 8
 
 # Every entry point include/rfattn.h declares.
 EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
-           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention", "rf_qkv_project")
+           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention", "rf_qkv_project",
+           "rf_set_frame_shift", "rf_add_frame_shift")
 
 
 class RfError(RuntimeError):
@@ -88,6 +89,10 @@ def lib():
         L.rf_window_attention.restype = i32
         L.rf_qkv_project.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, vp, i64, i64, i32, vp]
         L.rf_qkv_project.restype = i32
+        L.rf_set_frame_shift.argtypes = [vp, vp, i64]
+        L.rf_set_frame_shift.restype = i32
+        L.rf_add_frame_shift.argtypes = [vp, vp, i64, vp]
+        L.rf_add_frame_shift.restype = i32
         _lib = L
     return _lib
 
@@ -149,6 +154,26 @@ class Context:
             self.close()
         except Exception:
             pass
+
+    def set_frame_shift(self, shift, max_shift):
+        """Every later launch on this context adds shift[0] (an int64 CUDA tensor, read
+        when its kernels run, clamped to 0..max_shift) to all its frame indices; None
+        turns it off.  For replaying one captured step as the following steps."""
+        if shift is None:
+            _check(lib().rf_set_frame_shift(self.handle, None, 0))
+            self._shift = None
+            return
+        if not isinstance(shift, torch.Tensor) or not shift.is_cuda or shift.dtype != torch.int64:
+            raise TypeError("shift must be an int64 CUDA tensor")
+        _check(lib().rf_set_frame_shift(self.handle, ctypes.c_void_p(shift.data_ptr()), max_shift))
+        self._shift = shift  # keep the memory alive while the context uses it
+
+    def add_frame_shift(self, shift, delta, stream=None):
+        """Enqueue shift[0] += delta (stream-ordered, capturable in a graph)."""
+        if not isinstance(shift, torch.Tensor) or not shift.is_cuda or shift.dtype != torch.int64:
+            raise TypeError("shift must be an int64 CUDA tensor")
+        _check(lib().rf_add_frame_shift(self.handle, ctypes.c_void_p(shift.data_ptr()), delta,
+                                        _stream(stream)))
 
     def rope3d_apply(self, x, t0, y=None, stream=None):
         """y = 3D-RoPE(x) for token-major bf16 x whose first token is in frame t0."""

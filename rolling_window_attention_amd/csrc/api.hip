@@ -28,6 +28,8 @@ struct rf_ctx {
   RopeTables tab;
   int max_workers;    // persistent attention work-groups: kWorkersPerCu per CU
   float* d_partial;   // attention workspace: 2 * max_workers partial results
+  const int64_t* d_shift;  // device frame shift added by every launch (NULL: none)
+  int64_t max_shift;       // its clamp, validated against the tables
 };
 
 namespace {
@@ -176,6 +178,8 @@ rf_status rf_create(const rf_geom* g, rf_ctx** out) {
   c->d_tab = d;
   c->max_workers = max_workers;
   c->d_partial = part;
+  c->d_shift = nullptr;
+  c->max_shift = 0;
   c->tab.t = d;
   c->tab.h = d + off_h;
   c->tab.w = d + off_w;
@@ -206,7 +210,7 @@ rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* 
   if ((st = check_tensor(y, y_ld, row, "y")) != RF_OK) return st;
   if (x == y && x_ld != y_ld) return fail(RF_ERR_SHAPE, "in-place RoPE needs y_ld == x_ld");
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
-  if (t0 < 0 || t0 + (n_tokens - 1) / N >= g.max_frame)
+  if (t0 < 0 || t0 + (n_tokens - 1) / N + ctx->max_shift >= g.max_frame)
     return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
                 (long long)(t0 + (n_tokens - 1) / N), (long long)g.max_frame);
   RopeArgs a;
@@ -220,6 +224,7 @@ rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* 
   a.gw = g.grid_w;
   a.H = g.n_heads;
   a.tab = ctx->tab;
+  a.fs = {ctx->d_shift, ctx->max_shift};
   hipError_t e = launch_rope3d(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "rope3d launch");
   return RF_OK;
@@ -265,7 +270,7 @@ rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, i
   if ((st = check_tensor(v_new, v_ld, row, "v_new")) != RF_OK) return st;
   rf_kvcache after;
   if ((st = rf_kvcache_plan_roll(c, t0, n_frames, &after)) != RF_OK) return st;
-  if (t0 < 0 || t0 + n_frames > g.max_frame)
+  if (t0 < 0 || t0 + n_frames + ctx->max_shift > g.max_frame)
     return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
                 (long long)(t0 + n_frames - 1), (long long)g.max_frame);
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
@@ -288,6 +293,7 @@ rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, i
   a.gw = g.grid_w;
   a.H = g.n_heads;
   a.tab = ctx->tab;
+  a.fs = {ctx->d_shift, ctx->max_shift};
   hipError_t e = launch_roll(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kvcache roll launch");
   c->first = after.first;
@@ -310,7 +316,7 @@ rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_
     return fail(RF_ERR_SHAPE, "row strides must be at most 2^22 elements");
   rf_kvcache after;
   if ((st = rf_kvcache_plan_roll(c, t0, n_frames, &after)) != RF_OK) return st;
-  if (t0 < 0 || t0 + n_frames > g.max_frame)
+  if (t0 < 0 || t0 + n_frames + ctx->max_shift > g.max_frame)
     return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
                 (long long)(t0 + n_frames - 1), (long long)g.max_frame);
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
@@ -341,10 +347,39 @@ rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_
   a.inv_n = 1.0f / (float)N;
   a.inv_gw = 1.0f / (float)g.grid_w;
   a.tab = ctx->tab;
+  a.fs = {ctx->d_shift, ctx->max_shift};
   hipError_t e = launch_qkv_proj(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
   c->first = after.first;
   c->count = after.count;
+  return RF_OK;
+}
+
+rf_status rf_set_frame_shift(rf_ctx* ctx, const int64_t* d_shift, int64_t max_shift) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if (!d_shift) {
+    ctx->d_shift = nullptr;
+    ctx->max_shift = 0;
+    return RF_OK;
+  }
+  if ((reinterpret_cast<uintptr_t>(d_shift) & 7u) != 0) return fail(RF_ERR_ALIGN, "d_shift is not 8-byte aligned");
+  if (max_shift < 0 || max_shift >= ctx->g.max_frame)
+    return fail(RF_ERR_RANGE, "max_shift must be in 0..max_frame-1");
+  ctx->d_shift = d_shift;
+  ctx->max_shift = max_shift;
+  return RF_OK;
+}
+
+rf_status rf_add_frame_shift(const rf_ctx* ctx, int64_t* d_shift, int64_t delta, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if (!d_shift) return fail(RF_ERR_NULL, "d_shift is NULL");
+  if ((reinterpret_cast<uintptr_t>(d_shift) & 7u) != 0) return fail(RF_ERR_ALIGN, "d_shift is not 8-byte aligned");
+  hipError_t e = launch_add_shift(d_shift, delta, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "frame shift launch");
   return RF_OK;
 }
 
@@ -373,7 +408,7 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
     if ((st = check_tensor(s.o, s.o_ld, row, "o")) != RF_OK) return st;
     if (s.q_frames < 1 || s.ctx_frames < 1) return fail(RF_ERR_SHAPE, "segment %d: frames must be >= 1", i);
     if ((int64_t)s.q_frames * N >= kMaxTokens) return fail(RF_ERR_SHAPE, "segment %d: too many query tokens", i);
-    if (s.q_t0 < 0 || s.q_t0 + s.q_frames > g.max_frame)
+    if (s.q_t0 < 0 || s.q_t0 + s.q_frames + ctx->max_shift > g.max_frame)
       return fail(RF_ERR_RANGE, "segment %d: query frames outside the tables", i);
     if (s.ctx_t0 < c->first || s.ctx_t0 + s.ctx_frames > c->first + c->count)
       return fail(RF_ERR_RANGE, "segment %d: context %lld..%lld outside the window %lld..%lld", i,
@@ -421,6 +456,7 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   a.H = g.n_heads;
   a.c_log2 = scale * 1.4426950408889634f;
   a.tab = ctx->tab;
+  a.fs = {ctx->d_shift, ctx->max_shift};
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
   return RF_OK;

@@ -17,6 +17,19 @@ constexpr int kWorkersPerCu = 1;   // persistent attention work-groups per CU
 constexpr int kPartRows = kAttnBlockM;
 constexpr int kPartFloats = kPartRows * kHeadDim + 2 * kPartRows;
 
+// Frame shift of a steady-state step replayed from a graph: *p (device memory,
+// read when the kernel runs) clamped to [0, max], added to every absolute frame
+// index of the launch (RoPE positions, ring slots); 0 when p is null.
+struct FrameShift {
+  const int64_t* p;
+  int64_t max;
+};
+__device__ __forceinline__ int64_t frame_shift(const FrameShift& s) {
+  if (!s.p) return 0;
+  const int64_t v = *s.p;
+  return v < 0 ? 0 : (v > s.max ? s.max : v);
+}
+
 struct RopeArgs {
   const uint16_t* x;
   uint16_t* y;
@@ -24,6 +37,7 @@ struct RopeArgs {
   int64_t t0, n_tokens;
   int N, gw, H;
   RopeTables tab;
+  FrameShift fs;
 };
 
 struct RollArgs {
@@ -37,6 +51,7 @@ struct RollArgs {
   int slot0;             // t0 % W
   int n_frames, W, N, gw, H;
   RopeTables tab;
+  FrameShift fs;
 };
 
 struct SegDev {
@@ -67,6 +82,7 @@ struct AttnArgs {
   float c_log2;          // scale * log2(e)
   float* partial;        // workspace: 2 * n_workers partial results of kPartFloats
   RopeTables tab;
+  FrameShift fs;
 };
 
 // Fused QKV projection: y = x W^T, q token-major, k rotated into K ring slots,
@@ -86,6 +102,7 @@ struct ProjArgs {
   int n_workers;         // persistent work-groups: one per CU, a multiple of 8
   float inv_n, inv_gw;   // 1/N, 1/gw for the exact small divisions
   RopeTables tab;
+  FrameShift fs;
 };
 
 hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s);
@@ -94,5 +111,6 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 hipError_t prepare_window_attn();  // once per device, before the first launch
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
 hipError_t prepare_qkv_proj();     // once per device, before the first launch
+hipError_t launch_add_shift(int64_t* p, int64_t delta, hipStream_t s);
 
 }  // namespace rfattn

@@ -249,6 +249,9 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
 
   const int N = a.N;
   const int64_t head_elems = (int64_t)N * kHeadDim;
+  const int64_t sh = frame_shift(a.fs);
+  int slot0 = a.slot0 + (int)(sh % a.W);
+  if (slot0 >= a.W) slot0 -= a.W;
   if (part == 0) {
     // token rows: 32 chunks of 8 features each
     for (int idx = tid; idx < kTile * 32; idx += kThreads) {
@@ -266,9 +269,9 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
       uint32_t pin, col;
       const uint32_t fr = small_div((uint32_t)mg, (uint32_t)N, a.inv_n, &pin);
       const uint32_t row = small_div(pin, (uint32_t)a.gw, a.inv_gw, &col);
-      int slot = a.slot0 + (int)fr;
+      int slot = slot0 + (int)fr;
       if (slot >= a.W) slot -= a.W;  // slot0 < W and fr < W
-      const ChunkCS cs = rope_chunk_cs_of(a.tab, 4 * cc, a.t0 + fr, (int)row, (int)col);
+      const ChunkCS cs = rope_chunk_cs_of(a.tab, 4 * cc, a.t0 + sh + fr, (int)row, (int)col);
       uint16_t* kdst = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)pin * kHeadDim + 8 * cc;
 #pragma unroll
       for (int hh = 0; hh < kTile / kHeadDim; ++hh) {
@@ -286,7 +289,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
       const u32x4 v = *(const u32x4*)(T + fl * kORow + 8 * c);
       uint32_t n0;
       const uint32_t fr = small_div((uint32_t)(m0 + 8 * c), (uint32_t)N, a.inv_n, &n0);
-      int slot = a.slot0 + (int)fr;
+      int slot = slot0 + (int)fr;
       if (slot >= a.W) slot -= a.W;
       const int f = fl0 + fl;
       const int h = f / kHeadDim, d = f - h * kHeadDim;

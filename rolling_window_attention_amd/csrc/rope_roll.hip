@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a, uint32
   if (tl >= n) return;
   const uint32_t tok = tok_base + tl;
   const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
-  const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col);
+  const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + frame_shift(a.fs) + p.f, (int)p.row, (int)p.col);
   uint16_t* yrow = a.y + (int64_t)tok * a.y_ld + c * 8;
   rotate_heads(a.x + (int64_t)tok * a.x_ld + c * 8, h0, min(h0 + kRopeHpt, a.H), cs,
                [&](int h, u32x4 y) { __builtin_nontemporal_store(y, (u32x4*)(yrow + h * 128)); });
@@ -145,9 +145,12 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks
     if (tl >= k_tokens) return;
     const uint32_t tok = tok_base + tl;
     const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
-    int slot = a.slot0 + (int)p.f;
-    if (slot >= a.W) slot -= a.W;  // slot0 < W and f < W
-    const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + p.f, (int)p.row, (int)p.col);
+    const int64_t sh = frame_shift(a.fs);
+    int slot = a.slot0 + (int)(sh % a.W);
+    if (slot >= a.W) slot -= a.W;
+    slot += (int)p.f;
+    if (slot >= a.W) slot -= a.W;  // both terms below W
+    const ChunkCS cs = rope_chunk_cs_of(a.tab, (int)c * 4, a.t0 + sh + p.f, (int)p.row, (int)p.col);
     const uint32_t n = tok - p.f * (uint32_t)a.N;
     uint16_t* krow = a.k_ring + (int64_t)slot * a.slot_elems + (int64_t)n * 128 + c * 8;  // head 0
     const int64_t head_stride = (int64_t)a.N * 128;
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks
   const uint32_t fh = fhd >> 1, dh = fhd & 1u;
   const int f = (int)fh / a.H;
   const int h = (int)fh - f * a.H;
-  int slot = a.slot0 + f;
+  int slot = a.slot0 + (int)(frame_shift(a.fs) % a.W);
+  if (slot >= a.W) slot -= a.W;
+  slot += f;
   if (slot >= a.W) slot -= a.W;
   const uint32_t t0 = b * (uint32_t)kVBlock;
   const uint32_t ng = (min((uint32_t)kVBlock, N - t0)) >> 3;  // 8-token groups in the block
@@ -219,6 +224,14 @@ hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// *p += delta on the stream (a one-thread kernel: stream-ordered and capturable).
+__global__ void add_shift_kernel(int64_t* p, int64_t delta) { p[threadIdx.x] += delta; }
+
+hipError_t launch_add_shift(int64_t* p, int64_t delta, hipStream_t s) {
+  hipLaunchKernelGGL(add_shift_kernel, dim3(1), dim3(1), 0, s, p, delta);
+  return hipGetLastError();
 }
 
 }  // namespace rfattn

@@ -209,7 +209,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     for (int s = 0; s < 8; ++s) {
       const int c = 2 * s + hf;
       u32x4 x = *(const u32x4*)(qrow + 8 * c);
-      qf[s] = as_bf16x8(rope_chunk_scaled(x, 4 * c, sg.q_t0 + f, row, col, a.tab, cl64));
+      qf[s] = as_bf16x8(rope_chunk_scaled(x, 4 * c, sg.q_t0 + frame_shift(a.fs) + f, row, col, a.tab, cl64));
     }
   } else {
 #pragma unroll
@@ -248,7 +248,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     const int key0 = ka * kBlockN;
     const int f0 = key0 / N;
     kn = key0 - f0 * N;
-    kslot = (sg.ctx_slot0 + f0) % W;
+    kslot = (sg.ctx_slot0 + (int)(frame_shift(a.fs) % W) + f0) % W;
   }
   int kload = ka;
   int vslot = kslot, vn = kn, vload = ka;
