@@ -258,7 +258,7 @@ def main():
     # ---- extras (not part of the timed steps): denoise-only launch, the cache-update
     # pass alone, standalone RoPE, cold/warm single calls, the 30-step dynamic fill ----
     denoise_ms = rope_ms = update_ms = None
-    dynamic = projection = None
+    dynamic = projection = replay = None
     cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
@@ -290,6 +290,7 @@ def main():
         update_ms = e0.elapsed_time(e1) / reps
         dynamic = dynamic_fill(rf, ctx, W, N, H, D, pool, stream)
         projection = qkv_projection(rf, synth, g, ctx, W, stream)
+        replay = graph_replay(rf, synth, g, W, pool)
 
         # cold (a 1 GiB fill evicts L2 and the 256 MB MALL before each rep) and warm
         # single-call times of the standalone RoPE and of the step's roll; the roll
@@ -389,6 +390,8 @@ def main():
         out["dynamic_30_steps"] = dynamic
     if projection is not None:
         out["qkv_projection_16"] = projection
+    if replay is not None:
+        out["graph_replay_30_steps"] = replay
 
     if not args.no_cpu_baseline:
         ctx_frames = [written[t] for t in range(last_s - 6, last_s + 15)]
@@ -476,6 +479,78 @@ def qkv_projection(rf, synth, g, ctx, W, stream, reps=10):
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "library_gemm_only_ms": round(lib_ms, 4)}
+
+
+def graph_replay(rf, synth, g, W, pool, steps=30):
+    """The batched window step run eagerly for 30 steps, then captured once (with the
+    device frame shift and its increment) and replayed for the next 30 steps, on a
+    context of its own.  GPU time per step (events around each stretch) and host time
+    to enqueue a step (the Python loop without the final synchronisation)."""
+    import torch
+
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ctx = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, max_frame=8192)
+    cache = rf.KVCache(ctx, W)
+    cfg = synth.WORKLOAD_IDS["batched"]
+    cache.roll(up(synth.frames(g, cfg, 0, 0, W, synth.K + synth.CLEAN)),
+               up(synth.frames(g, cfg, 0, 0, W, synth.V + synth.CLEAN)), 0)
+    p = pool[0]
+    oa = torch.empty((15 * N, H, D), dtype=torch.bfloat16, device=dev)
+    ob = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+
+    def step(s):
+        cache.roll(p["k"], p["v"], s - 1)
+        rf.window_attention(ctx, cache, [rf.Segment(p["qa"], s, oa, s - 6, 21),
+                                         rf.Segment(p["qb"], s - 1, ob, s - 6, 21)])
+
+    s = 7
+    for _ in range(3):
+        step(s)
+        s += 1
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(steps):
+        step(s)
+        s += 1
+    host_eager = (time.perf_counter() - h0) / steps
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gpu_eager = e0.elapsed_time(e1) / steps
+
+    shift = torch.zeros(1, dtype=torch.int64, device=dev)
+    ctx.set_frame_shift(shift, steps + 1)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(s)
+            ctx.add_frame_shift(shift, 1)
+    stream.wait_stream(side)
+    graph.replay()  # step s, untimed
+    torch.cuda.synchronize()
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    host_graph = (time.perf_counter() - h0) / steps
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gpu_graph = e0.elapsed_time(e1) / steps
+    assert int(shift.item()) == steps + 1
+    ctx.set_frame_shift(None, 0)
+    return {"steps": steps, "gpu_ms_per_step_eager": round(gpu_eager, 4),
+            "gpu_ms_per_step_graph": round(gpu_graph, 4),
+            "host_us_per_step_eager": round(host_eager * 1e6, 1),
+            "host_us_per_step_graph": round(host_graph * 1e6, 1)}
 
 
 def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
