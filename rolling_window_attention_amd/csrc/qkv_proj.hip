@@ -34,12 +34,6 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef RF_QKV_WAVES
-#define RF_QKV_WAVES 8
-#endif
-#ifndef RF_QKV_SGB
-#define RF_QKV_SGB 1
-#endif
 
 namespace rfattn {
 
@@ -51,7 +45,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = RF_QKV_WAVES;     // 4 (one per SIMD) or 8 (two per SIMD)
+// Eight waves (two per SIMD) of 128 x 64: four waves of 128 x 128 (one per SIMD)
+// fill all 256 accumulation registers of a wave and ran slower.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;               // tokens and features per tile
 constexpr int kBW = kTile / (kWaves / 2);  // B-side columns per wave: 128 or 64
@@ -72,16 +68,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-#ifndef RF_QKV_NT
-#define RF_QKV_NT 1
-#endif
-// Output stores: non-temporal (the outputs are not read again by this kernel).
-__device__ __forceinline__ void out_store(u32x4* p, u32x4 v) {
-  if (RF_QKV_NT)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
-}
+// Output stores: non-temporal (the outputs are not read again by this kernel;
+// measured 6-10% faster than ordinary stores for the whole kernel).
+__device__ __forceinline__ void out_store(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 // Work-group id -> tile index, each XCD walking a contiguous run (a bijection).
 __device__ __forceinline__ int xcd_tile(int bid, int total) {
@@ -173,9 +162,9 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
   // One reduction step on LDS buffer kt & 1; with `more`, the next step's global
   // loads are issued during the first substep's MFMAs and staged into the other
   // buffer during the last one.  Each substep's MFMAs run while the next
-  // substep's fragments are read.  With RF_QKV_SGB the interleave is fixed with
-  // scheduling groups: one fragment read, global load or staging write after
-  // each MFMA.
+  // substep's fragments are read.  The interleave is fixed with scheduling
+  // groups: one fragment read, global load or staging write after each MFMA
+  // (left to the compiler, the reads sat right before their MFMAs: 4% slower).
   auto kstep = [&](int kt, auto more) {
     constexpr bool kMore = decltype(more)::value;
     constexpr int kSub = kStepK / 16;
@@ -207,7 +196,6 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
           acc[ia][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][ia], bfr[set][ib], acc[ia][ib], 0, 0, 0);
     }
     if constexpr (kMore) stage((kt + 1) & 1);
-#if RF_QKV_SGB
     __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);  // substep 0's fragments first
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
@@ -219,7 +207,6 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
         if (kMore && s == kSub - 1 && i < kVm) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
     }
-#endif
   };
   for (int kt = 0; kt + 1 < nk; ++kt) {
     kstep(kt, std::true_type{});

@@ -12,15 +12,6 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef RF_ROPE_BATCH
-#define RF_ROPE_BATCH 3
-#endif
-#ifndef RF_ROPE_HPT
-#define RF_ROPE_HPT 3
-#endif
-#ifndef RF_V_BLOCK
-#define RF_V_BLOCK 128
-#endif
 
 namespace rfattn {
 
@@ -47,8 +38,8 @@ __device__ __forceinline__ TokPos tok_pos(uint32_t tok, uint32_t N, float inv_n,
 
 constexpr int kRopeThreads = 256;
 constexpr int kRopeRows = kRopeThreads / 16;     // (token, head group) rows per work-group
-constexpr int kRopeHpt = RF_ROPE_HPT;            // heads per thread (a head group)
-constexpr int kRopeBatch = RF_ROPE_BATCH;        // head chunks loaded before the first is rotated
+constexpr int kRopeHpt = 3;                      // heads per thread (a head group)
+constexpr int kRopeBatch = 3;                    // head chunks loaded before the first is rotated
 
 // Row R of the [tokens][head groups] grid -> token and the group's first head.
 __device__ __forceinline__ void rope_row(uint32_t R, int H, uint32_t* tok, int* h0) {
@@ -128,7 +119,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // N = 1560): 65 instead of 69 us for the 16-frame roll.  Work-groups owning
 // fewer dims per token read partial lines that a work-group on another XCD
 // fetches again, which measured much slower.
-constexpr int kVBlock = RF_V_BLOCK;  // tokens per value work-group (multiple of 8)
+constexpr int kVBlock = 128;  // tokens per value work-group (multiple of 8)
 static_assert(kVBlock % 8 == 0, "value block");
 
 // Work-groups [0, v_blocks): value blocks as above.  Work-groups from v_blocks
