@@ -44,11 +44,12 @@
 // outside these statements names a0..a63.  The compiler does not see either
 // that the statements are MFMAs, so they carry their own wait states: two
 // before an MFMA whose operand the VALU may just have written (the weights P,
-// -m), eighteen or more between the last MFMA writing a register and the first
-// VALU or memory instruction touching it.  The build also scans the generated
-// assembly for any instruction (its own or the compiler's) that touches an
-// MFMA result, or feeds an MFMA a VALU result, with fewer wait states than
-// those two rules require.
+// -m), and 20 (the scores) or 24 (O^T at the end) between the last MFMA writing
+// a register and the first VALU instruction reading it.  The build also scans
+// the generated assembly for any instruction (its own or the compiler's) that
+// touches an MFMA result with fewer than 12 wait states (what the compiler
+// itself inserts for these MFMAs), or feeds an MFMA a VALU result with fewer
+// than 2.
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so a row max needs one cross-half exchange, the row sum
 // none until the end, and the rescale is a per-lane scalar.  The key order
