@@ -15,20 +15,23 @@
 // multi-head self-attention; the pages do not print it.
 //
 // Tiling.  A work-group computes a 256-token x 256-feature tile over the whole
-// reduction (C = 1,536: 24 steps of 64), four waves of 128 x 128 each, 16
-// accumulator blocks of 32 x 32 per wave (v_mfma_f32_32x32x16_bf16).  Both
-// operand tiles (256 rows x 64 k of x and of W, k contiguous) are staged
-// through LDS in two buffers: the next step's global loads are issued before
-// the current step's MFMAs and written to the other buffer after them.  The
-// product is computed transposed for q and k tiles (A = W, B = x: a lane ends
-// with 4 consecutive features of one token, i.e. two rotation pairs) and
-// plainly for v tiles (A = x, B = W: 4 consecutive tokens of one feature, the
-// order of a value row in the ring).  Either way the epilogue writes the
-// accumulators as bf16 into an LDS image whose rows are the B-side index, and
-// copies it out in 16-byte chunks: token rows of 256 features for q and k (k
+// reduction (C = 1,536: 24 steps of 64), eight waves of 128 x 64 each (two per
+// SIMD), 8 accumulator blocks of 32 x 32 per wave (v_mfma_f32_32x32x16_bf16).
+// Both operand tiles (256 rows x 64 k of x and of W, k contiguous) are staged
+// through LDS in two buffers: the next step's global loads are issued during
+// the current step's first MFMAs and written to the other buffer during its
+// last ones, and each substep's MFMAs run while the next substep's fragments are
+// read, in an order fixed with scheduling groups.  The product is computed
+// transposed for q and k tiles (A = W, B = x: a lane ends with 4 consecutive
+// features of one token, i.e. two rotation pairs) and plainly for v tiles
+// (A = x, B = W: 4 consecutive tokens of one feature, the order of a value row
+// in the ring).  Either way the epilogue writes the accumulators as bf16 into an
+// LDS image whose rows are the B-side index, and copies it out in 16-byte
+// chunks with non-temporal stores: token rows of 256 features for q and k (k
 // rotated on the way, with the roll's arithmetic), feature rows of 256 tokens
-// for v.  Tiles are numbered so that each XCD walks consecutive feature tiles
-// of one token tile (x rows reused from L2).
+// for v.  One persistent work-group per CU walks the tiles, numbered so that
+// each XCD walks consecutive feature tiles of one token tile (x rows reused from
+// L2), and puts the next tile's first loads in flight before its epilogue.
 #include <type_traits>
 
 #include "device_common.h"
