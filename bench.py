@@ -297,8 +297,10 @@ def main():
         # rewrites the last step's own frames, so the ring contents do not change
         flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
         p_last = pool[(last_s - s0) % args.pool]
+        # the 1-frame roll rewrites the last step's newest frame (s+14) in place
         single = {"rope3d_q": lambda: ctx.rope3d_apply(p["qa"], last_s, y=qr),
-                  "roll_16": lambda: cache.roll(p_last["k"], p_last["v"], last_s - 1)}
+                  "roll_16": lambda: cache.roll(p_last["k"], p_last["v"], last_s - 1),
+                  "roll_1": lambda: cache.roll(p_last["k"][15 * N:], p_last["v"][15 * N:], last_s + 14)}
         cold_warm = {}
         for name, fn in single.items():
             cold, warm = [], []
@@ -373,7 +375,7 @@ def main():
             "tokens": 15 * N, "ms": round(rope_ms, 4),
             "GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes}
+        nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes, "roll_1": roll_bytes // 16}
         out["cold_warm"] = {
             name: {"bytes": nbytes[name], "cold_ms": round(c, 4), "warm_ms": round(w, 4),
                    "cold_hbm_frac": round(nbytes[name] / (c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
