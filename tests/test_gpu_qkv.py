@@ -210,3 +210,30 @@ def test_projection_errors():
     assert e.value.status == 4
     torch.cuda.synchronize()
     assert (cache.first, cache.count) == (0, 2)
+
+
+def test_strided_operands_match_dense_bit_exact():
+    """x, w and q with row strides larger than C (views into wider buffers) give the
+    same q and ring contents, bit for bit, as dense tensors; 4 frames into an empty
+    4-frame ring (n_frames = capacity)."""
+    g = synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4)
+    N, H, D, W = g.tokens_per_frame, g.n_heads, g.head_dim, g.window
+    C = H * D
+    x = synth.layer_input(g, 15, 0, 0, 4)
+    w = synth.qkv_weight(g, 15)
+    ctx = _ctx(g)
+    dense, strided = rf.KVCache(ctx, W), rf.KVCache(ctx, W)
+    q_dense = torch.empty((4 * N, H, D), dtype=torch.bfloat16, device="cuda")
+    dense.project(up(x), up(w), q_dense, 0)
+    xw = torch.zeros((4 * N, C + 72), dtype=torch.bfloat16, device="cuda")
+    xw[:, :C] = up(x)
+    ww = torch.zeros((3 * C, C + 40), dtype=torch.bfloat16, device="cuda")
+    ww[:, :C] = up(w)
+    qw = torch.zeros((4 * N, C + 24), dtype=torch.bfloat16, device="cuda")
+    strided.project(xw[:, :C], ww[:, :C], qw[:, :C], 0)
+    torch.cuda.synchronize()
+    assert (strided.first, strided.count) == (dense.first, dense.count) == (0, 4)
+    assert np.array_equal(down(qw[:, :C]), down(q_dense).reshape(4 * N, C))
+    assert not down(qw[:, C:]).any(), "the padding of q was written"
+    assert np.array_equal(down(strided.k), down(dense.k))
+    assert np.array_equal(down(strided.v), down(dense.v))
