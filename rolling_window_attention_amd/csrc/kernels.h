@@ -13,7 +13,8 @@ constexpr int kMaxSegments = 8;
 constexpr int kAttnBlockM = 256;   // query rows per attention work item
 constexpr int kAttnBlockN = 64;    // keys per key tile (one work unit per key tile)
 constexpr int kWorkersPerCu = 1;   // persistent attention work-groups per CU
-// One partial result of a split query tile: O [rows][head_dim], m [rows], l [rows].
+// One partial result of a split query tile: unnormalised O as [head_dim / 8][rows][8]
+// (dims 8c .. 8c+7 of every row in chunk c), then m [rows], l [rows].
 constexpr int kPartRows = kAttnBlockM;
 constexpr int kPartFloats = kPartRows * kHeadDim + 2 * kPartRows;
 

@@ -570,15 +570,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
         }
       }
     }
-  } else {  // piece of a split tile: unnormalised O [row][dim], then m[row], l[row]
+  } else {  // piece of a split tile: unnormalised O [chunk][row][8], then m[row], l[row]
+    // Chunk c = 4 dt + g4 holds dims 32 dt + 8 g4 + 0..7 of every row, so one store
+    // instruction of a wave (32 rows x both halves) writes 1 KB contiguous.
     const int r = wave * 32 + lr;  // row inside the query tile
-    float* orow = part + r * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 w = {o[dt][4 * g4 + 0], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
-        *(f32x4*)(orow + 32 * dt + 8 * g4 + 4 * hf) = w;
+        *(f32x4*)(part + ((4 * dt + g4) * kPartRows + r) * 8 + 4 * hf) = w;
       }
     if (hf == 0) {
       part[kPartRows * kHeadDim + r] = m_run;
@@ -647,7 +648,12 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
 // range and continue past it: worker v holds the first piece (in its slot 0
 // if the tile starts its range, else slot 1), the following workers the
 // next pieces (their slot 0).  O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i.
+// Thread t merges row t/2, dims 8c + 4(t%2) + 0..3 of every chunk c: the loads
+// of a wave read 1 KB contiguous.  The bf16 rows are staged in LDS (16-byte
+// chunk c of row r at position c ^ (r mod 16)) and written 256 bytes per row.
 __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
+  constexpr int kChunks = kHeadDim / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t img[kPartRows * kHeadDim];
   const uint32_t P = (uint32_t)a.n_workers;
   const uint32_t span = a.total_units - a.sk_unit_begin;
   const uint32_t v = blockIdx.x;
@@ -662,41 +668,45 @@ __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
   if (t0 < r0 || t1 <= r1) return;  // started in an earlier range, or not split
   const int h = (int)tl / sg.q_tiles;
   const int qt = (int)tl - h * sg.q_tiles;
-  const int r = threadIdx.x >> 1;           // row inside the query tile
-  const int d0 = (threadIdx.x & 1) * 64;    // half of the head dimension
-  const int qi = qt * kBlockM + r;
-  if (qi >= sg.q_tokens) return;
+  const int r = threadIdx.x >> 1;  // row inside the query tile
+  const int jh = threadIdx.x & 1;  // which four of each chunk's eight dims
 
   float M = -INFINITY;
   for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
     const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
     M = fmaxf(M, p[kPartRows * kHeadDim + r]);
   }
-  float acc[64];
+  f32x4 acc[kChunks];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.0f;
+  for (int c = 0; c < kChunks; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
   for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
     const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
     const float sc = __builtin_amdgcn_exp2f(p[kPartRows * kHeadDim + r] - M);
     L += sc * p[kPartRows * kHeadDim + kPartRows + r];
-    const float* orow = p + r * kHeadDim + d0;
+    const float* src = p + r * 8 + 4 * jh;
 #pragma unroll
-    for (int i = 0; i < 64; i += 4) {
-      const f32x4 x = *(const f32x4*)(orow + i);
-      acc[i] += sc * x[0];
-      acc[i + 1] += sc * x[1];
-      acc[i + 2] += sc * x[2];
-      acc[i + 3] += sc * x[3];
+    for (int c = 0; c < kChunks; ++c) {
+      const f32x4 x = *(const f32x4*)(src + c * kPartRows * 8);
+      acc[c][0] += sc * x[0];
+      acc[c][1] += sc * x[1];
+      acc[c][2] += sc * x[2];
+      acc[c][3] += sc * x[3];
     }
   }
   const float inv = 1.0f / L;
-  uint16_t* out = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim + d0;
 #pragma unroll
-  for (int i = 0; i < 64; i += 8) {
-    u32x4 w = {pack2(acc[i] * inv, acc[i + 1] * inv), pack2(acc[i + 2] * inv, acc[i + 3] * inv),
-               pack2(acc[i + 4] * inv, acc[i + 5] * inv), pack2(acc[i + 6] * inv, acc[i + 7] * inv)};
-    *(u32x4*)(out + i) = w;
+  for (int c = 0; c < kChunks; ++c) {
+    const u32x2 w = {pack2(acc[c][0] * inv, acc[c][1] * inv), pack2(acc[c][2] * inv, acc[c][3] * inv)};
+    *(u32x2*)(img + r * kHeadDim + (c ^ (r & 15)) * 8 + 4 * jh) = w;
+  }
+  __syncthreads();
+  const int q = threadIdx.x & (kChunks - 1);  // 16-byte chunk of the row
+  for (int rr = threadIdx.x / kChunks; rr < kPartRows; rr += 2 * kPartRows / kChunks) {
+    const int qi = qt * kBlockM + rr;
+    if (qi < sg.q_tokens)
+      *(u32x4*)(sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim + q * 8) =
+          *(const u32x4*)(img + rr * kHeadDim + (q ^ (rr & 15)) * 8);
   }
 }
 
