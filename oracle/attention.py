@@ -47,10 +47,12 @@ def attend_head(qh, kh, vh, scale):
 
 
 def window_attention(q, q_t0, k, v, ctx_t0, grid_h, grid_w, pairs, base,
-                     scale=None, rows=None, block=256, workers=None):
+                     scale=None, rows=None, block=256, workers=None, q_tok0=0):
     """Attention of query tokens over context tokens, float64.
 
-    q      : [Lq, H, D] raw (un-rotated) queries of frames q_t0, q_t0+1, ...
+    q      : [Lq, H, D] raw (un-rotated) queries of frames q_t0, q_t0+1, ...,
+             the first being token q_tok0 of frame q_t0 (a block cut out of a
+             frame sequence at any token; 0 = whole frames)
     k, v   : [Lk, H, D] raw keys / values of the context frames ctx_t0, ...
              (Lk a whole number of frames)
     rows   : optional 1-D array of query-token indices to compute (sampling);
@@ -63,7 +65,7 @@ def window_attention(q, q_t0, k, v, ctx_t0, grid_h, grid_w, pairs, base,
     L, H, D = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    qh_all = rope3d.rope_exact(q, q_t0, grid_h, grid_w, pairs, base)
+    qh_all = rope3d.rope_exact(q, q_t0, grid_h, grid_w, pairs, base, tok0=q_tok0)
     if rows is not None:
         qh_all = qh_all[np.asarray(rows, dtype=np.int64)]
     kh_all = rope3d.rope_exact(k, ctx_t0, grid_h, grid_w, pairs, base)

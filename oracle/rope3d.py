@@ -12,7 +12,10 @@ below are the plainest ones and are listed in the design doc:
 * Token ``i`` of a block that starts at absolute latent frame ``t0`` sits at
   ``(t, r, c) = (t0 + i // N, (i % N) // grid_w, i % grid_w)``, ``N =
   grid_h * grid_w`` (frame-major, row-major inside a frame).  ``t`` is the
-  absolute frame index, never re-based as the window rolls.
+  absolute frame index, never re-based as the window rolls.  A block may
+  start inside its first frame, at token ``tok0`` of it (a sequence split
+  cuts frames; positions are per token): then ``i`` is replaced by
+  ``tok0 + i`` above.
 * The head dimension is split into ``D/2`` rotation pairs ``(2p, 2p+1)``
   (interleaved).  The first ``P_t`` pairs rotate by the time position, the
   next ``P_h`` by the row, the last ``P_w`` by the column.
@@ -41,10 +44,13 @@ import numpy as np
 from . import bf16
 
 
-def token_positions(t0, n_tokens, grid_h, grid_w):
-    """(t, r, c) int64 arrays for ``n_tokens`` consecutive tokens from frame ``t0``."""
+def token_positions(t0, n_tokens, grid_h, grid_w, tok0=0):
+    """(t, r, c) int64 arrays for ``n_tokens`` consecutive tokens from token
+    ``tok0`` of frame ``t0``."""
     n = grid_h * grid_w
-    i = np.arange(n_tokens, dtype=np.int64)
+    if not 0 <= tok0 < n:
+        raise ValueError("tok0 must lie inside the first frame")
+    i = tok0 + np.arange(n_tokens, dtype=np.int64)
     t = t0 + i // n
     r = (i % n) // grid_w
     c = i % grid_w
@@ -80,9 +86,9 @@ def angle_table(positions, n_pairs, base, f32=False):
     return C, S
 
 
-def pair_cos_sin(t0, n_tokens, grid_h, grid_w, pairs, base, f32=False):
+def pair_cos_sin(t0, n_tokens, grid_h, grid_w, pairs, base, f32=False, tok0=0):
     """cos, sin of every rotation pair of every token: two [n_tokens, D/2] arrays."""
-    t, r, c = token_positions(t0, n_tokens, grid_h, grid_w)
+    t, r, c = token_positions(t0, n_tokens, grid_h, grid_w, tok0)
     Ct, St = angle_table(t, pairs[0], base, f32)
     Ch, Sh = angle_table(r, pairs[1], base, f32)
     Cw, Sw = angle_table(c, pairs[2], base, f32)
@@ -98,15 +104,16 @@ def _check(x, pairs):
         raise ValueError("head_dim must equal 2 * sum(pairs)")
 
 
-def rope_exact(x, t0, grid_h, grid_w, pairs, base):
-    """Rotate float64 ``x`` [L, H, D] (token-major) in float64.
+def rope_exact(x, t0, grid_h, grid_w, pairs, base, tok0=0):
+    """Rotate float64 ``x`` [L, H, D] (token-major, first token = token ``tok0`` of
+    frame ``t0``) in float64.
 
     y_{2p}   = x_{2p} cos - x_{2p+1} sin
     y_{2p+1} = x_{2p} sin + x_{2p+1} cos
     """
     x = np.asarray(x, dtype=np.float64)
     _check(x, pairs)
-    C, S = pair_cos_sin(t0, x.shape[0], grid_h, grid_w, pairs, base, f32=False)
+    C, S = pair_cos_sin(t0, x.shape[0], grid_h, grid_w, pairs, base, f32=False, tok0=tok0)
     C = C[:, None, :]
     S = S[:, None, :]
     x0 = x[:, :, 0::2]

@@ -88,8 +88,9 @@ def test_rows_subset_matches_full():
     assert np.allclose(full[rows], sub, rtol=0, atol=1e-15)
 
 
-def _brute(q, q_t0, k, v, ctx_t0, gh, gw, pairs, base):
-    """Pure-Python loops: RoPE pair by pair from the formulas, then softmax attention."""
+def _brute(q, q_t0, k, v, ctx_t0, gh, gw, pairs, base, q_tok0=0):
+    """Pure-Python loops: RoPE pair by pair from the formulas, then softmax attention.
+    Query token i sits at token q_tok0 + i counted from the start of frame q_t0."""
     n = gh * gw
 
     def pos(t0, i):
@@ -113,7 +114,7 @@ def _brute(q, q_t0, k, v, ctx_t0, gh, gw, pairs, base):
     for h in range(Hh):
         kr = [rot(list(k[j, h]), pos(ctx_t0, j)) for j in range(Lk)]
         for i in range(Lq):
-            qr = rot(list(q[i, h]), pos(q_t0, i))
+            qr = rot(list(q[i, h]), pos(q_t0, q_tok0 + i))
             s = [sum(qr[d] * kr[j][d] for d in range(Dd)) / math.sqrt(Dd) for j in range(Lk)]
             m = max(s)
             e = [math.exp(x - m) for x in s]
@@ -133,6 +134,32 @@ def test_brute_force_tiny():
     o = attention.window_attention(q, 3, k, v, 1, gh, gw, pairs, BASE, workers=1)
     want = _brute(q, 3, k, v, 1, gh, gw, pairs, BASE)
     assert np.allclose(o, want, rtol=0, atol=1e-13)
+
+
+def test_brute_force_token_offset():
+    # a query block starting at token 4 of frame 3 (of 6) and running into frame 4
+    gh, gw, pairs = 2, 3, (2, 2, 2)
+    n = gh * gw
+    q = _rand((5, 2, 12), 27)
+    k = _rand((4 * n, 2, 12), 28)
+    v = _rand((4 * n, 2, 12), 29)
+    o = attention.window_attention(q, 3, k, v, 1, gh, gw, pairs, BASE, workers=1, q_tok0=4)
+    want = _brute(q, 3, k, v, 1, gh, gw, pairs, BASE, q_tok0=4)
+    assert np.allclose(o, want, rtol=0, atol=1e-13)
+
+
+def test_token_offset_rows_equal_whole_frame_rows():
+    # rows are independent: a block cut at token 29 of frame 2 gives the same rows as
+    # the whole frames 2..4 it was cut from
+    q = _rand((3 * N, H, D), 30)
+    k = _rand((5 * N, H, D), 31)
+    v = _rand((5 * N, H, D), 32)
+    full = attention.window_attention(q, 2, k, v, 0, GH, GW, PAIRS, BASE)
+    part = attention.window_attention(q[29:29 + 70], 2, k, v, 0, GH, GW, PAIRS, BASE, q_tok0=29)
+    assert np.allclose(full[29:29 + 70], part, rtol=0, atol=1e-15)
+    # and a block starting in a later frame is the same as one at offset tok0 + N
+    late = attention.window_attention(q[N + 5:N + 40], 3, k, v, 0, GH, GW, PAIRS, BASE, q_tok0=5)
+    assert np.allclose(full[N + 5:N + 40], late, rtol=0, atol=1e-15)
 
 
 def test_brute_force_full_head_dim():

@@ -55,6 +55,15 @@ def test_positions_frame_major_row_major():
     assert (t[2 * N + 5 * GW + 3], r[2 * N + 5 * GW + 3], c[2 * N + 5 * GW + 3]) == (9, 5, 3)
 
 
+def test_positions_with_token_offset():
+    # a block cut out of the frame sequence at token N-2 of frame 7
+    t, r, c = rope3d.token_positions(7, 5, GH, GW, tok0=N - 2)
+    got = list(zip(t.tolist(), r.tolist(), c.tolist()))
+    assert got == [(7, GH - 1, GW - 2), (7, GH - 1, GW - 1), (8, 0, 0), (8, 0, 1), (8, 0, 2)]
+    with pytest.raises(ValueError):
+        rope3d.token_positions(7, 5, GH, GW, tok0=N)
+
+
 def _complex_axis(z, pos, n_pairs):
     """Independent 1-D RoPE: pair j of the axis times exp(i pos 10000^(-j/P))."""
     j = np.arange(n_pairs)
