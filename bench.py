@@ -216,13 +216,11 @@ def main():
             ev[2].record(stream)
         step_idx[0] += 1
 
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-
     # Shader clock under this load: the firmware metrics refresh too slowly for the
     # short timed loop, so sample during ~1.5 s of the same steps first (untimed) and
-    # keep the samples of the last second.
+    # keep the samples of the last second.  This runs before the warm-up steps:
+    # stopping the sampler idles the GPU for tens of ms, after which the clock needs
+    # a few launches to come back up, and the warm-up steps absorb that.
     clock = ClockSampler(period_s=0.005)
     sclk = None
     if clock.ok and not args.no_clock:
@@ -237,6 +235,8 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        run_step()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -258,7 +258,7 @@ def main():
     # ---- extras (not part of the timed steps): denoise-only launch, the cache-update
     # pass alone, standalone RoPE, cold/warm single calls, the 30-step dynamic fill ----
     denoise_ms = rope_ms = update_ms = None
-    dynamic = projection = replay = None
+    dynamic = projection = replay = share = None
     cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
@@ -290,6 +290,7 @@ def main():
         update_ms = e0.elapsed_time(e1) / reps
         dynamic = dynamic_fill(rf, ctx, W, N, H, D, pool, stream)
         projection = qkv_projection(rf, synth, g, ctx, W, stream)
+        share = hybrid_share(rf, synth, W, stream)
         replay = graph_replay(rf, synth, g, W, pool)
 
         # cold (a 1 GiB fill evicts L2 and the 256 MB MALL before each rep) and warm
@@ -392,6 +393,8 @@ def main():
         out["dynamic_30_steps"] = dynamic
     if projection is not None:
         out["qkv_projection_16"] = projection
+    if share is not None:
+        out["hybrid_share_3_heads"] = share
     if replay is not None:
         out["graph_replay_30_steps"] = replay
 
@@ -481,6 +484,50 @@ def qkv_projection(rf, synth, g, ctx, W, stream, reps=10):
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "library_gemm_only_ms": round(lib_ms, 4)}
+
+
+def hybrid_share(rf, synth, W, stream, reps=10):
+    """One device's share of the heads x sequence split over eight devices: 3 of the 12
+    heads and the second half of a batched step's queries -- denoise tokens 11,700..23,399
+    (from token 780 of the step's eighth frame) and cache-update tokens 780..1,559 -- in
+    one launch over 21 context frames (32,760 keys).  Synthetic 3-head ring and queries."""
+    import torch
+
+    g = synth.SHARD
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    cfg = synth.WORKLOAD_IDS["shard"]
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ctx = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, 4096)
+    cache = rf.KVCache(ctx, W)
+    s = 9
+    cache.roll(up(synth.frames(g, cfg, s, s - 6, W, synth.K)),
+               up(synth.frames(g, cfg, s, s - 6, W, synth.V)), s - 6)
+    half = N // 2
+    qa = up(synth.frames(g, cfg, s, s + 7, 8, synth.Q)[half:])   # 11,700 tokens
+    qb = up(synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)[half:])
+    oa, ob = torch.empty_like(qa), torch.empty_like(qb)
+    segs = [rf.Segment(qa, s + 7, oa, s - 6, W, q_tok0=half),
+            rf.Segment(qb, s - 1, ob, s - 6, W, q_tok0=half)]
+    for _ in range(2):
+        rf.window_attention(ctx, cache, segs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        rf.window_attention(ctx, cache, segs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nq = qa.shape[0] + qb.shape[0]
+    flops = 4.0 * nq * W * N * H * D
+    del cache, ctx
+    return {"heads": H, "q_tokens": [qa.shape[0], qb.shape[0]], "kv_tokens": W * N, "ms": round(ms, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def graph_replay(rf, synth, g, W, pool, steps=30):

@@ -53,8 +53,9 @@ class KVCacheDesc(ctypes.Structure):
 
 class SegmentDesc(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("q_ld", ctypes.c_int64), ("o", ctypes.c_void_p),
-                ("o_ld", ctypes.c_int64), ("q_t0", ctypes.c_int64), ("q_frames", ctypes.c_int32),
-                ("ctx_frames", ctypes.c_int32), ("ctx_t0", ctypes.c_int64)]
+                ("o_ld", ctypes.c_int64), ("q_t0", ctypes.c_int64), ("q_tok0", ctypes.c_int32),
+                ("q_tokens", ctypes.c_int32), ("ctx_t0", ctypes.c_int64), ("ctx_frames", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -248,10 +249,13 @@ class KVCache:
 
 
 class Segment:
-    """Query tokens q (frames q_t0..) attending to context frames ctx_t0..ctx_t0+ctx_frames-1."""
+    """Query tokens q attending to context frames ctx_t0..ctx_t0+ctx_frames-1.  q's first
+    token is token q_tok0 of frame q_t0 (0 for whole frames); q and o hold any number
+    of tokens."""
 
-    def __init__(self, q, q_t0, o, ctx_t0, ctx_frames):
+    def __init__(self, q, q_t0, o, ctx_t0, ctx_frames, q_tok0=0):
         self.q, self.q_t0, self.o, self.ctx_t0, self.ctx_frames = q, q_t0, o, ctx_t0, ctx_frames
+        self.q_tok0 = q_tok0
 
 
 def window_attention(ctx, cache, segments, scale=0.0, stream=None):
@@ -262,10 +266,9 @@ def window_attention(ctx, cache, segments, scale=0.0, stream=None):
     for i, s in enumerate(segments):
         qp, qld, nq = _token_major(s.q, "q", ctx.n_heads, ctx.head_dim)
         op, old, no = _token_major(s.o, "o", ctx.n_heads, ctx.head_dim)
-        if nq != no or nq % ctx.tokens_per_frame:
-            raise ValueError("q and o must hold the same whole number of frames")
-        arr[i] = SegmentDesc(qp, qld, op, old, s.q_t0, nq // ctx.tokens_per_frame, s.ctx_frames,
-                             s.ctx_t0)
+        if nq != no:
+            raise ValueError("q and o must hold the same number of tokens")
+        arr[i] = SegmentDesc(qp, qld, op, old, s.q_t0, s.q_tok0, nq, s.ctx_t0, s.ctx_frames, 0)
     _check(lib().rf_window_attention(ctx.handle, ctypes.byref(cache.desc), arr, len(segments),
                                      scale, _stream(stream)))
 

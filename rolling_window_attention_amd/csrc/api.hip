@@ -406,9 +406,14 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
     const rf_attn_segment& s = segs[i];
     if ((st = check_tensor(s.q, s.q_ld, row, "q")) != RF_OK) return st;
     if ((st = check_tensor(s.o, s.o_ld, row, "o")) != RF_OK) return st;
-    if (s.q_frames < 1 || s.ctx_frames < 1) return fail(RF_ERR_SHAPE, "segment %d: frames must be >= 1", i);
-    if ((int64_t)s.q_frames * N >= kMaxTokens) return fail(RF_ERR_SHAPE, "segment %d: too many query tokens", i);
-    if (s.q_t0 < 0 || s.q_t0 + s.q_frames + ctx->max_shift > g.max_frame)
+    if (s.q_tokens < 1 || s.ctx_frames < 1)
+      return fail(RF_ERR_SHAPE, "segment %d: q_tokens and ctx_frames must be >= 1", i);
+    if (s.q_tok0 < 0 || s.q_tok0 >= N)
+      return fail(RF_ERR_SHAPE, "segment %d: q_tok0 %d outside 0..%lld", i, (int)s.q_tok0, (long long)(N - 1));
+    if (s.reserved != 0) return fail(RF_ERR_SHAPE, "segment %d: reserved must be 0", i);
+    if ((int64_t)s.q_tokens >= kMaxTokens) return fail(RF_ERR_SHAPE, "segment %d: too many query tokens", i);
+    const int64_t q_span = ((int64_t)s.q_tok0 + s.q_tokens + N - 1) / N;  // frames the queries touch
+    if (s.q_t0 < 0 || s.q_t0 + q_span + ctx->max_shift > g.max_frame)
       return fail(RF_ERR_RANGE, "segment %d: query frames outside the tables", i);
     if (s.ctx_t0 < c->first || s.ctx_t0 + s.ctx_frames > c->first + c->count)
       return fail(RF_ERR_RANGE, "segment %d: context %lld..%lld outside the window %lld..%lld", i,
@@ -420,7 +425,8 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
     d.q_ld = s.q_ld;
     d.o_ld = s.o_ld;
     d.q_t0 = s.q_t0;
-    d.q_tokens = (int)(s.q_frames * N);
+    d.q_tok0 = s.q_tok0;
+    d.q_tokens = s.q_tokens;
     d.q_tiles = (d.q_tokens + kAttnBlockM - 1) / kAttnBlockM;
     d.ctx_keys = (int)(s.ctx_frames * N);
     d.ctx_slot0 = (int)mod(s.ctx_t0, c->capacity);

@@ -60,7 +60,8 @@ struct SegDev {
   uint16_t* o;
   int64_t q_ld, o_ld;
   int64_t q_t0;          // frame of the first query token
-  int q_tokens;          // q_frames * N
+  int q_tok0;            // the first query token's index inside frame q_t0
+  int q_tokens;          // query tokens (rows of q and o)
   int q_tiles;           // ceil(q_tokens / kAttnBlockM)
   int ctx_keys;          // ctx_frames * N
   int ctx_slot0;         // ring slot of the first context frame

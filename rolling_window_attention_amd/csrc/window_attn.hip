@@ -200,8 +200,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const bool qvalid = qi < sg.q_tokens;
   bf16x8 qf[8];
   if (qvalid) {
-    const int f = qi / a.N;
-    const int pin = qi - f * a.N;
+    const int pos = qi + sg.q_tok0;  // token index counted from the start of frame q_t0
+    const int f = pos / a.N;
+    const int pin = pos - f * a.N;
     const int row = pin / a.gw;
     const int col = pin - row * a.gw;
     const uint16_t* qrow = sg.q + (int64_t)qi * sg.q_ld + h * kHeadDim;

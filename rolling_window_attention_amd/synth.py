@@ -41,7 +41,11 @@ FULL = Geometry()
 # The tiny case: 6x8 grid (48 tokens per frame), 5-frame window.
 TINY = Geometry(grid_h=6, grid_w=8, window=5)
 
-WORKLOAD_IDS = {"tiny": 1, "cache_update": 2, "denoise": 3, "dynamic": 4, "batched": 5}
+# One GPU's share of the hybrid heads x sequence split over eight devices: 3 of the 12
+# heads (its query half is a token range of the full step's queries).
+SHARD = Geometry(n_heads=3)
+
+WORKLOAD_IDS = {"tiny": 1, "cache_update": 2, "denoise": 3, "dynamic": 4, "batched": 5, "shard": 7}
 
 
 def f32_to_bf16_bits(x):

@@ -74,15 +74,16 @@ class RotatedKeys:
             del self.cache[key]
 
 
-def oracle_rows(geom, q_bits, q_t0, kh_frames, v_frames, rows, scale=None):
+def oracle_rows(geom, q_bits, q_t0, kh_frames, v_frames, rows, scale=None, q_tok0=0):
     """Oracle attention for selected query rows, from pre-rotated context keys.
 
     kh_frames: list of float64 [N, H, D] rotated keys (oracle rope_exact) of the context
-    frames in order; v_frames: list of bf16 bit arrays [N, H, D]."""
+    frames in order; v_frames: list of bf16 bit arrays [N, H, D]; q_bits' first token is
+    token q_tok0 of frame q_t0."""
     g = geom
     kh = np.concatenate(kh_frames, axis=0)
     v = np.concatenate([f64(x) for x in v_frames], axis=0)
-    qh = orope.rope_exact(f64(q_bits), q_t0, g.grid_h, g.grid_w, g.pairs, g.base)[rows]
+    qh = orope.rope_exact(f64(q_bits), q_t0, g.grid_h, g.grid_w, g.pairs, g.base, tok0=q_tok0)[rows]
     D = q_bits.shape[2]
     if scale is None:
         scale = 1.0 / np.sqrt(D)

@@ -110,3 +110,24 @@ def test_plan_roll_rejects_bad_descriptors(L):
         rf.plan_roll(0, 0, 0, 0, 1)
     with pytest.raises(rf.RfError):
         rf.plan_roll(5, 0, 6, 0, 1)
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes structures have the C structures' sizes and field offsets (the header
+    compiled by the host C compiler)."""
+    pairs = [(rf.Geom, "rf_geom"), (rf.KVCacheDesc, "rf_kvcache"), (rf.SegmentDesc, "rf_attn_segment")]
+    lines = ["#include <stddef.h>", "#include <stdio.h>", f'#include "{HEADER}"', "int main(void) {"]
+    for cls, cname in pairs:
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    assert os.system(f"gcc -std=c11 -o {exe} {src}") == 0
+    got = dict(l.rsplit(" ", 1) for l in os.popen(str(exe)).read().splitlines())
+    for cls, cname in pairs:
+        assert int(got[f"{cname} size"]) == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert int(got[f"{cname} {field}"]) == getattr(cls, field).offset, (cname, field)

@@ -164,10 +164,10 @@ def _fill_steady(g, cfg, s, cache):
     return data
 
 
-def _check_rows(g, rk, data, q_bits, q_t0, o, ctx_lo, ctx_hi, rows, what):
+def _check_rows(g, rk, data, q_bits, q_t0, o, ctx_lo, ctx_hi, rows, what, q_tok0=0):
     khs = [rk.get(t, data[t][2], data[t][0]) for t in range(ctx_lo, ctx_hi)]
     vs = [data[t][1] for t in range(ctx_lo, ctx_hi)]
-    want = oracle_rows(g, q_bits, q_t0, khs, vs, rows)
+    want = oracle_rows(g, q_bits, q_t0, khs, vs, rows, q_tok0=q_tok0)
     got = f64(down(o))[rows]
     assert_close(got, want, what)
 
@@ -288,6 +288,70 @@ def test_dynamic_window_fill_30_steps():
         _check_rows(g, rk, data, q, s, o, lo, s + 15, rows, f"dynamic step {s}")
 
 
+def test_token_offset_segments_tiny():
+    """Query blocks cut at any token, in one launch: 70 rows from token 29 of frame 2 (into
+    frame 4) and 35 rows from token 5 of frame 1, over frames 0..4; every row checked."""
+    g, cfg = synth.TINY, 61
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    k = synth.frames(g, cfg, 0, 0, 5, synth.K)
+    v = synth.frames(g, cfg, 0, 0, 5, synth.V)
+    q = synth.frames(g, cfg, 0, 0, 5, synth.Q)
+    cache.roll(up(k), up(v), 0)
+    qa, qb = q[2 * N + 29:2 * N + 99], q[N + 5:N + 40]
+    oa = torch.empty((70, H, D), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty((35, H, D), dtype=torch.bfloat16, device="cuda")
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), 2, oa, 0, 5, q_tok0=29),
+                                     rf.Segment(up(qb), 1, ob, 0, 5, q_tok0=5)])
+    torch.cuda.synchronize()
+    args = (f64(k), f64(v), 0, g.grid_h, g.grid_w, g.pairs, g.base)
+    assert_close(f64(down(oa)), oatt.window_attention(f64(qa), 2, *args, q_tok0=29), "from token 29")
+    assert_close(f64(down(ob)), oatt.window_attention(f64(qb), 1, *args, q_tok0=5), "from token 5")
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_one_gpu_share_of_the_hybrid_split_full_size(half):
+    """One device's share of the heads x sequence split: 3 heads, and one half of the
+    step's queries -- denoise tokens 11,700 h .. 11,700 h + 11,699 of frames s..s+14 (the
+    second half starts at token 780 of frame s+7) and cache-update tokens 780 h .. 780 h
+    + 779 of frame s-1 -- in one launch over the 21-frame window; sampled rows."""
+    g, cfg = synth.SHARD, synth.WORKLOAD_IDS["shard"]
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    s = 9
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    _fill_steady(g, cfg, s - 1, cache)
+    data = {}
+    for t in range(s - 6, s):
+        data[t] = (synth.frame(g, cfg, t + 1, t, synth.K + synth.CLEAN),
+                   synth.frame(g, cfg, t + 1, t, synth.V + synth.CLEAN), ("clean", t + 1))
+    for t in range(s, s + 15):
+        data[t] = (synth.frame(g, cfg, s, t, synth.K), synth.frame(g, cfg, s, t, synth.V),
+                   ("noisy", s))
+    cache.roll(up(np.concatenate([data[t][0] for t in range(s - 1, s + 15)])),
+               up(np.concatenate([data[t][1] for t in range(s - 1, s + 15)])), s - 1)
+    na, nb = 15 * N // 2, N // 2
+    qa = synth.frames(g, cfg, s, s, 15, synth.Q)[half * na:(half + 1) * na]
+    qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)[half * nb:(half + 1) * nb]
+    a_t0, a_tok0 = s + (half * na) // N, (half * na) % N
+    b_tok0 = half * nb
+    oa = torch.empty((na, H, D), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty((nb, H, D), dtype=torch.bfloat16, device="cuda")
+    print(f"share {half}: denoise from frame {a_t0} token {a_tok0}, update from token {b_tok0}",
+          flush=True)
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), a_t0, oa, s - 6, 21, q_tok0=a_tok0),
+                                     rf.Segment(up(qb), s - 1, ob, s - 6, 21, q_tok0=b_tok0)])
+    torch.cuda.synchronize()
+    rk = RotatedKeys(g)
+    rows_a = np.union1d(sample_rows(na, N, extra=64, seed=20 + half),
+                        [N - a_tok0 - 1, N - a_tok0])  # both sides of the first frame edge
+    _check_rows(g, rk, data, qa, a_t0, oa, s - 6, s + 15, rows_a, f"share {half} denoise",
+                q_tok0=a_tok0)
+    _check_rows(g, rk, data, qb, s - 1, ob, s - 6, s + 15, sample_rows(nb, N, extra=32, seed=30),
+                f"share {half} cache update", q_tok0=b_tok0)
+
+
 def test_attention_errors():
     g = synth.TINY
     ctx = _ctx(g)
@@ -308,3 +372,18 @@ def test_attention_errors():
     assert e.value.status == 3
     with pytest.raises(ValueError):
         rf.window_attention(ctx, cache, [])
+    N = g.tokens_per_frame
+    for tok0 in (-1, N):  # the first token must lie inside frame q_t0
+        with pytest.raises(rf.RfError) as e:
+            rf.window_attention(ctx, cache, [rf.Segment(q[:5], 0, o[:5], 0, 3, q_tok0=tok0)])
+        assert e.value.status == 3
+    with pytest.raises(ValueError):  # q and o of different lengths
+        rf.window_attention(ctx, cache, [rf.Segment(q[:5], 0, o[:6], 0, 3)])
+    small = _ctx(g, max_frame=20)
+    cs = rf.KVCache(small, g.window)
+    cs.roll(k, k, 0)
+    rf.window_attention(small, cs, [rf.Segment(q[:2], 19, o[:2], 0, 3, q_tok0=N - 2)])  # frame 19 only
+    with pytest.raises(rf.RfError) as e:  # token N-1 of frame 19, then frame 20: beyond the tables
+        rf.window_attention(small, cs, [rf.Segment(q[:2], 19, o[:2], 0, 3, q_tok0=N - 1)])
+    assert e.value.status == 4
+    torch.cuda.synchronize()
