@@ -12,6 +12,7 @@ flops 4*Lq*Lk*H*D of both segments / step time); `roofline` is the attention ker
 own rate from HIP events on the launch stream against the dense bf16 MFMA peak.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -576,6 +577,7 @@ def graph_replay(rf, synth, g, W, pool, steps=30):
 
     shift = torch.zeros(1, dtype=torch.int64, device=dev)
     ctx.set_frame_shift(shift, steps + 1)
+    gc.collect()  # free unreachable contexts now, not inside the capture
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -650,8 +652,21 @@ def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
         "sample": f"{n_rows} of 23,400 denoise query rows x 12 heads over 32,760 keys of the last "
                   f"timed step (incl. rotating the 21 context frames), fp64 numpy",
         "seconds": round(secs, 2),
+        "cpu_model": host_cpu_model(),
         "parity_rows": {"max_abs": float(err.max()), "mean_abs": float(err.mean()), "rel_l2": rel},
     }
+
+
+def host_cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -89,7 +89,9 @@ typedef struct rf_ctx rf_ctx;
 rf_status rf_create(const rf_geom* g, rf_ctx** out);
 
 /* Free a context (NULL is ignored).  The caller must first make sure no work
- * that uses it is still queued. */
+ * that uses it is still queued.  It frees device memory, which is not
+ * allowed while a stream of the device is being captured into a graph (the
+ * capture is invalidated): destroy contexts outside captures. */
 void rf_destroy(rf_ctx* ctx);
 
 /* Human-readable name of a status code (static storage). */

@@ -126,12 +126,25 @@ def _token_major(t, name, n_heads, head_dim):
     return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.shape[0]
 
 
+_pending_destroy = []
+
+
+def _destroy_pending():
+    """rf_destroy the handles of closed contexts, unless a graph capture is under way on
+    the current stream."""
+    if not _pending_destroy or torch.cuda.is_current_stream_capturing():
+        return
+    while _pending_destroy:
+        lib().rf_destroy(_pending_destroy.pop())
+
+
 class Context:
     """Geometry + device RoPE tables (rf_create / rf_destroy)."""
 
     def __init__(self, grid_h=30, grid_w=52, n_heads=12, head_dim=128, pairs=(22, 21, 21),
                  base=10000.0, max_frame=4096):
         g = Geom(grid_h, grid_w, n_heads, head_dim, (ctypes.c_int32 * 3)(*pairs), base, max_frame)
+        _destroy_pending()
         h = ctypes.c_void_p()
         _check(lib().rf_create(ctypes.byref(g), ctypes.byref(h)))
         self._h = h
@@ -146,9 +159,14 @@ class Context:
         return self._h
 
     def close(self):
+        """Free the context (rf_destroy).  While the current stream is being captured
+        into a graph, freeing device memory would invalidate the capture, so the handle
+        is then kept and freed at the next close or Context creation outside a capture
+        (this happens when the garbage collector runs inside a capture)."""
         if getattr(self, "_h", None) is not None:
-            lib().rf_destroy(self._h)
+            _pending_destroy.append(self._h)
             self._h = None
+        _destroy_pending()
 
     def __del__(self):
         try:

@@ -8,6 +8,8 @@ segment (query frame s-1), both over the window's last W frames.  The graph hold
 launches of step s0 and a shift increment; replay i is step s0 + i.  Inputs are the
 same tensors every step (their pointers are baked into the graph).
 """
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -46,6 +48,9 @@ def _run(g, n_new, replays, cfg):
     shift = torch.zeros(1, dtype=torch.int64, device="cuda")
     contexts[1].set_frame_shift(shift, replays)
     torch.cuda.synchronize()
+    # contexts of earlier tests that sit in reference cycles (exception tracebacks) are
+    # freed now rather than by a collection inside the capture
+    gc.collect()
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -93,3 +98,37 @@ def test_frame_shift_validation():
     assert e.value.status == 4
     ctx.set_frame_shift(None, 0)
     cache.roll(kv, kv, 7)                     # without the shift: fine
+
+
+def test_context_collected_inside_a_capture_is_freed_after_it():
+    """A context that is garbage when the collector runs inside a graph capture is not
+    freed there (freeing device memory would invalidate the capture) but at the next
+    context creation outside it."""
+    g = synth.TINY
+    gc.collect()  # contexts left in cycles by earlier tests are closed now, outside a capture
+    ctx = rf.Context(g.grid_h, g.grid_w, g.n_heads, g.head_dim, g.pairs, g.base, 64)
+    assert not rf._pending_destroy
+    cycle = [ctx]
+    cycle.append(cycle)  # only the cyclic collector can free it now
+    del ctx, cycle
+    x = torch.zeros(16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gc.disable()
+    try:
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                x.add_(1)
+                gc.collect()  # closes the context while the capture is under way
+                pending = len(rf._pending_destroy)
+                x.add_(1)
+    finally:
+        gc.enable()
+    torch.cuda.current_stream().wait_stream(side)
+    assert pending == 1
+    graph.replay()
+    torch.cuda.synchronize()
+    assert float(x[0]) == 2.0
+    rf.Context(g.grid_h, g.grid_w, g.n_heads, g.head_dim, g.pairs, g.base, 64).close()
+    assert not rf._pending_destroy
