@@ -187,7 +187,7 @@ def main():
         qa = np.concatenate([synth.frame(g, cfg, s, t, synth.Q) for t in range(s, s + 15)])
         qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
         pool.append(dict(k=up(np.concatenate(ks)), v=up(np.concatenate(vs)), qa=up(qa), qb=up(qb)))
-        pool_bits.append((ks, vs, qa))
+        pool_bits.append((ks, vs, qa, qb))
     oa = torch.empty((15 * N, H, D), dtype=torch.bfloat16, device=dev)
     ob = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -203,7 +203,7 @@ def main():
     def run_step(ev=None):
         s = step_idx[0]
         p = pool[(s - s0) % args.pool]
-        ks, vs, _ = pool_bits[(s - s0) % args.pool]
+        ks, vs, _, _ = pool_bits[(s - s0) % args.pool]
         for j in range(16):
             written[s - 1 + j] = (ks[j], vs[j])
         if ev:
@@ -300,9 +300,23 @@ def main():
         flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
         p_last = pool[(last_s - s0) % args.pool]
         # the 1-frame roll rewrites the last step's newest frame (s+14) in place
+        # a plain device copy of the 1-frame roll's bytes (9.6 MB read + 9.6 MB written):
+        # what one launch of that size costs at best
+        c_src = torch.empty(N * H * D * 2, dtype=torch.bfloat16, device=dev)
+        c_dst = torch.empty_like(c_src)
         single = {"rope3d_q": lambda: ctx.rope3d_apply(p["qa"], last_s, y=qr),
                   "roll_16": lambda: cache.roll(p_last["k"], p_last["v"], last_s - 1),
-                  "roll_1": lambda: cache.roll(p_last["k"][15 * N:], p_last["v"][15 * N:], last_s + 14)}
+                  "roll_1": lambda: cache.roll(p_last["k"][15 * N:], p_last["v"][15 * N:], last_s + 14),
+                  "copy_roll_1_bytes": lambda: c_dst.copy_(c_src)}
+        # Each timed call is enqueued while the GPU is still busy (behind the flush, or
+        # behind torch's bounded spin kernel for the warm call), so the events measure the
+        # GPU's time and not the host's launch latency on an idle GPU.
+        def busy():
+            try:
+                torch.cuda._sleep(100000)
+            except Exception:
+                pass
+
         cold_warm = {}
         for name, fn in single.items():
             cold, warm = [], []
@@ -310,10 +324,11 @@ def main():
                 flush.zero_()
                 e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
                 cold.append(e0.elapsed_time(e1))
+                busy()
                 e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
                 warm.append(e0.elapsed_time(e1))
             cold_warm[name] = (float(np.median(cold)), float(np.median(warm)))
-        del flush
+        del flush, c_src, c_dst
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
@@ -377,7 +392,8 @@ def main():
             "tokens": 15 * N, "ms": round(rope_ms, 4),
             "GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes, "roll_1": roll_bytes // 16}
+        nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes, "roll_1": roll_bytes // 16,
+                  "copy_roll_1_bytes": roll_bytes // 16}
         out["cold_warm"] = {
             name: {"bytes": nbytes[name], "cold_ms": round(c, 4), "warm_ms": round(w, 4),
                    "cold_hbm_frac": round(nbytes[name] / (c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -401,8 +417,8 @@ def main():
 
     if not args.no_cpu_baseline:
         ctx_frames = [written[t] for t in range(last_s - 6, last_s + 15)]
-        qa_bits = pool_bits[(last_s - s0) % args.pool][2]
-        out["cpu_baseline"] = cpu_baseline(args, g, last_s, ctx_frames, qa_bits, oa)
+        _, _, qa_bits, qb_bits = pool_bits[(last_s - s0) % args.pool]
+        out["cpu_baseline"] = cpu_baseline(args, g, last_s, ctx_frames, qa_bits, oa, qb_bits, ob)
 
     print(json.dumps(out), flush=True)
 
@@ -604,12 +620,13 @@ def graph_replay(rf, synth, g, W, pool, steps=30):
             "host_us_per_step_graph": round(host_graph * 1e6, 1)}
 
 
-def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
+def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa, qb_bits, ob):
     """The fp64 oracle timed on the host cores on a bounded sample of the same workload:
     R query rows of the denoise segment (all 12 heads) over the full 32,760-key window,
     including the oracle's rotation of the context keys.  Scaled to TFLOP/s by the sampled
     rows' algorithmic flops.  The sampled rows also give a parity spot check of the last
-    timed step."""
+    timed step.  The step's cache-update segment (1,560 rows, the cache-update pass on its
+    own) is timed in full beside it, with its own parity check."""
     import torch
     from threadpoolctl import threadpool_limits
 
@@ -644,6 +661,17 @@ def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
     got = obf.bits_to_f64(oa.view(torch.int16).cpu().numpy().view(np.uint16))[rows]
     err = np.abs(got - o)
     rel = float(np.linalg.norm((got - o).ravel()) / np.linalg.norm(o.ravel()))
+
+    # the cache-update segment in full: queries of frame s-1 over the same window
+    qb = obf.bits_to_f64(qb_bits)
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1, user_api="blas"):
+        o_b = oatt.window_attention(qb, s - 1, k, v, s - 6, g.grid_h, g.grid_w, g.pairs, g.base,
+                                    block=64, workers=workers)
+    secs_b = time.perf_counter() - t0
+    got_b = obf.bits_to_f64(ob.view(torch.int16).cpu().numpy().view(np.uint16))
+    rel_b = float(np.linalg.norm((got_b - o_b).ravel()) / np.linalg.norm(o_b.ravel()))
+    flops_b = 4.0 * N * lk * H * D
     return {
         "value": round(flops / secs / 1e12, 6),
         "unit": "TFLOP/s",
@@ -654,6 +682,11 @@ def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa):
         "seconds": round(secs, 2),
         "cpu_model": host_cpu_model(),
         "parity_rows": {"max_abs": float(err.max()), "mean_abs": float(err.mean()), "rel_l2": rel},
+        "cache_update_pass": {"rows": N, "seconds": round(secs_b, 2),
+                              "TFLOP/s": round(flops_b / secs_b / 1e12, 6),
+                              "parity": {"max_abs": float(np.abs(got_b - o_b).max()),
+                                         "mean_abs": float(np.abs(got_b - o_b).mean()),
+                                         "rel_l2": rel_b}},
     }
 
 
