@@ -248,6 +248,53 @@ def test_batched_two_phase_step_full_size():
                 "batched B")
 
 
+def test_batched_step_full_size_every_row_and_canaries():
+    """One full check of the batched step (s = 7): every one of the 23,400 + 1,560 output
+    rows x 12 heads against the oracle, with canaries -- rows before and after each output
+    and 16 padding columns per row, filled with a sentinel -- that must survive."""
+    from threadpoolctl import threadpool_limits
+    g, cfg = synth.FULL, 57
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    s = 7
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    _fill_steady(g, cfg, s - 1, cache)
+    data = {}
+    for t in range(s - 6, s):
+        data[t] = (synth.frame(g, cfg, t + 1, t, synth.K + synth.CLEAN),
+                   synth.frame(g, cfg, t + 1, t, synth.V + synth.CLEAN))
+    for t in range(s, s + 15):
+        data[t] = (synth.frame(g, cfg, s, t, synth.K), synth.frame(g, cfg, s, t, synth.V))
+    cache.roll(up(np.concatenate([data[t][0] for t in range(s - 1, s + 15)])),
+               up(np.concatenate([data[t][1] for t in range(s - 1, s + 15)])), s - 1)
+    qa = synth.frames(g, cfg, s, s, 15, synth.Q)
+    qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
+    pad, row = 3, H * D
+    sentinel = -12345  # bf16 bits 0xCFC7, a value no output row holds
+
+    def canaried(n):
+        full = torch.full((n + 2 * pad, row + 16), sentinel, dtype=torch.int16, device="cuda")
+        return full, full.view(torch.bfloat16)[pad:pad + n, :row].view(n, H, D)
+
+    fa, oa = canaried(15 * N)
+    fb, ob = canaried(N)
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), s, oa, s - 6, 21),
+                                     rf.Segment(up(qb), s - 1, ob, s - 6, 21)])
+    torch.cuda.synchronize()
+    for full, n, what in ((fa, 15 * N, "A"), (fb, N, "B")):
+        f = full.cpu().numpy()
+        assert (f[:pad] == sentinel).all() and (f[pad + n:] == sentinel).all(), f"rows around {what} written"
+        assert (f[:, row:] == sentinel).all(), f"padding columns of {what} written"
+    k = f64(np.concatenate([data[t][0] for t in range(s - 6, s + 15)]))
+    v = f64(np.concatenate([data[t][1] for t in range(s - 6, s + 15)]))
+    print("oracle over all rows of both segments", flush=True)
+    with threadpool_limits(limits=1, user_api="blas"):
+        want_a = oatt.window_attention(f64(qa), s, k, v, s - 6, g.grid_h, g.grid_w, g.pairs, g.base)
+        want_b = oatt.window_attention(f64(qb), s - 1, k, v, s - 6, g.grid_h, g.grid_w, g.pairs, g.base)
+    assert_close(f64(down(oa)), want_a, "batched A, every row")
+    assert_close(f64(down(ob)), want_b, "batched B, every row")
+
+
 def test_dynamic_window_fill_30_steps():
     """30 steps in one process: context grows 15..21 frames as the ring fills, then one
     frame is evicted per step; no reallocation between steps.  Sampled rows every step."""
