@@ -126,6 +126,13 @@ def _token_major(t, name, n_heads, head_dim):
     return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.shape[0]
 
 
+def _check_shift(shift):
+    if not isinstance(shift, torch.Tensor) or not shift.is_cuda or shift.dtype != torch.int64:
+        raise TypeError("shift must be an int64 CUDA tensor")
+    if shift.numel() < 1:
+        raise ValueError("shift must hold at least one element")
+
+
 _pending_destroy = []
 
 
@@ -182,15 +189,13 @@ class Context:
             _check(lib().rf_set_frame_shift(self.handle, None, 0))
             self._shift = None
             return
-        if not isinstance(shift, torch.Tensor) or not shift.is_cuda or shift.dtype != torch.int64:
-            raise TypeError("shift must be an int64 CUDA tensor")
+        _check_shift(shift)
         _check(lib().rf_set_frame_shift(self.handle, ctypes.c_void_p(shift.data_ptr()), max_shift))
         self._shift = shift  # keep the memory alive while the context uses it
 
     def add_frame_shift(self, shift, delta, stream=None):
         """Enqueue shift[0] += delta (stream-ordered, capturable in a graph)."""
-        if not isinstance(shift, torch.Tensor) or not shift.is_cuda or shift.dtype != torch.int64:
-            raise TypeError("shift must be an int64 CUDA tensor")
+        _check_shift(shift)
         _check(lib().rf_add_frame_shift(self.handle, ctypes.c_void_p(shift.data_ptr()), delta,
                                         _stream(stream)))
 

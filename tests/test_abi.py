@@ -131,3 +131,17 @@ def test_binding_structs_match_the_header(tmp_path):
         assert int(got[f"{cname} size"]) == ctypes.sizeof(cls), cname
         for field, _ in cls._fields_:
             assert int(got[f"{cname} {field}"]) == getattr(cls, field).offset, (cname, field)
+
+
+def test_binding_rejects_host_and_wrong_typed_tensors():
+    """Pointers reach the kernels only from bf16 (or int16) device tensors of the right
+    shape; host tensors and other dtypes are refused before any library call."""
+    import torch
+    with pytest.raises(TypeError):
+        rf._token_major(torch.zeros((4, 12, 128), dtype=torch.bfloat16), "q", 12, 128)
+    with pytest.raises(TypeError):
+        rf._token_major(np.zeros((4, 12, 128), dtype=np.uint16), "q", 12, 128)
+    with pytest.raises(TypeError):
+        rf._check_shift(torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        rf._check_shift(None)
