@@ -444,6 +444,12 @@ def test_attention_errors():
         assert e.value.status == 3
     with pytest.raises(ValueError):  # q and o of different lengths
         rf.window_attention(ctx, cache, [rf.Segment(q[:5], 0, o[:6], 0, 3)])
+    with pytest.raises(rf.RfError) as e:  # an empty query segment: torch hands over a null
+        rf.window_attention(ctx, cache, [rf.Segment(q[:0], 0, o[:0], 0, 3)])  # pointer for it
+    assert e.value.status in (1, 3)  # RF_ERR_NULL, or RF_ERR_SHAPE for a non-null pointer
+    with pytest.raises(ValueError):  # more segments than one launch takes
+        rf.window_attention(ctx, cache, [rf.Segment(q[i:i + 1], 0, o[i:i + 1], 0, 3, q_tok0=i)
+                                         for i in range(rf.MAX_SEGMENTS + 1)])
     small = _ctx(g, max_frame=20)
     cs = rf.KVCache(small, g.window)
     cs.roll(k, k, 0)
