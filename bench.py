@@ -31,15 +31,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_attn_traffic.json")
 KERNEL_SOURCES = ["csrc/window_attn.hip", "csrc/device_common.h", "csrc/kernels.h", "build.py"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(package_dir=None):
     """Hash of what the attention kernel is made from (its sources and the build script,
     which sets its register split) without comments and blank lines, so a comment edit
     does not invalidate counter figures taken on the same code."""
     import re
+    package_dir = package_dir or os.path.join(ROOT, "rolling_window_attention_amd")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         comment = r"#.*" if name.endswith(".py") else r"//.*"
-        with open(os.path.join(ROOT, "rolling_window_attention_amd", name)) as f:
+        with open(os.path.join(package_dir, name)) as f:
             for line in f:
                 code = re.sub(comment, "", line).rstrip()
                 if code:
