@@ -98,9 +98,10 @@ struct TileRef {
 
 // Tiles are numbered in groups of kGroupM token tiles x all feature tiles, token
 // tile fastest inside a group: the 32 work-groups of an XCD (consecutive numbers)
-// then share about 4 token panels and 8 feature panels at each reduction step
-// instead of 2 and 18, so more of their operand reads hit the XCD's L2.
-constexpr int kGroupM = 4;
+// then share about 8 token panels and 4 feature panels at each reduction step
+// instead of 2 and 18, so more of their operand reads hit the XCD's L2.  (Group
+// sizes 2, 4, 8, 16 measured; 8 was fastest.)
+constexpr int kGroupM = 8;
 
 __device__ __forceinline__ TileRef tile_ref(const ProjArgs& a, int tile) {
   TileRef t;
