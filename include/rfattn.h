@@ -38,6 +38,18 @@
  *   - Token positions: token i of a block whose first frame is t0 is at
  *     (frame t0 + i/N, row (i%N)/grid_w, column i%grid_w), N = grid_h*grid_w.
  *     Frames are absolute latent frame indices in 0..max_frame-1.
+ *
+ * Notes for callers written against a plainer sketch of this interface
+ * (V ring [W][H][N][D], frame counts everywhere, one ld per call):
+ *   - the V ring is [W][H][D][N] (each slot transposed), so the value
+ *     product reads 8 consecutive keys of one dim as one 16-byte chunk; a
+ *     caller that inspects V slots transposes the last two axes;
+ *   - rf_rope3d_apply takes a token count (n_frames*N for whole frames) and
+ *     separate input and output strides (x_ld, y_ld);
+ *   - an rf_attn_segment names its queries as a token range (q_t0, q_tok0,
+ *     q_tokens): whole frames are q_tok0 = 0, q_tokens = n_frames*N;
+ *   - rf_geom.max_frame is the number of table rows (frames 0..max_frame-1),
+ *     i.e. the largest supported frame index plus one.
  */
 #ifndef RFATTN_H
 #define RFATTN_H
@@ -131,7 +143,13 @@ rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* 
  *      head's keys are contiguous for each dim.
  * The caller allocates both (capacity*H*N*D*2 bytes each, 16-byte aligned)
  * and zero-fills or otherwise initialises them; a new cache has count == 0.
- * The library reads and writes the descriptor only inside rf_kvcache_roll.
+ * The library reads and writes the descriptor only inside rf_kvcache_roll
+ * (and rf_qkv_project).
+ * Size limit: the attention kernel addresses each ring buffer with 32-bit
+ * byte offsets, so capacity*H*N*D*2 + 16 must not exceed 0x7FFFFFF0
+ * (2 GiB - 16 bytes): at most 448 slots at 30x52 tokens, 12 heads of 128.
+ * Every call that takes a ring returns RF_ERR_SHAPE for a larger one before
+ * anything is enqueued; rf_kvcache_bytes checks a capacity in advance.
  */
 typedef struct {
   void* k;
@@ -140,6 +158,15 @@ typedef struct {
   int32_t count;    /* 0..capacity */
   int64_t first;    /* oldest valid frame (any value while count == 0) */
 } rf_kvcache;
+
+/*
+ * rf_kvcache_bytes -- host-only: the size in bytes of one ring buffer (K or
+ * V) of `capacity` slots for geometry g, i.e. capacity*H*N*D*2.  Touches no
+ * device.  Errors: RF_ERR_NULL (g or bytes NULL), RF_ERR_SHAPE (invalid
+ * geometry as in rf_create, capacity < 1, or a ring beyond the size limit
+ * above).  *bytes is written only on RF_OK.
+ */
+rf_status rf_kvcache_bytes(const rf_geom* g, int32_t capacity, int64_t* bytes);
 
 /*
  * rf_kvcache_roll -- write n_frames new frames t0..t0+n_frames-1 into the
@@ -158,7 +185,8 @@ typedef struct {
  *
  * k_new, v_new: token-major [n_frames*N][ld] bf16, un-rotated.
  * Requires 1 <= n_frames <= capacity and, unless the ring is empty,
- * first <= t0 <= first+count (an empty ring starts its window at t0).
+ * first <= t0 <= first+count (an empty ring starts its window at t0); a ring
+ * beyond the size limit gives RF_ERR_SHAPE.
  * On RF_OK, *c's first/count are updated on the host after the kernel is
  * enqueued; on error *c is unchanged.  The caller serialises calls that
  * share a descriptor.
@@ -236,7 +264,8 @@ typedef struct {
  *
  * Errors: RF_ERR_NULL, RF_ERR_ALIGN, RF_ERR_SHAPE (n_segs outside
  * 1..RF_MAX_SEGMENTS, q_tokens/ctx_frames < 1, q_tok0 outside 0..N-1,
- * reserved != 0, ld too small), RF_ERR_RANGE (context not inside
+ * reserved != 0, ld too small, a ring beyond the size limit of
+ * rf_kvcache), RF_ERR_RANGE (context not inside
  * first..first+count-1, or query frames beyond the tables).  Output rows
  * must not overlap between segments.
  */

@@ -39,11 +39,9 @@ def softmax_rows(s):
 
 
 def attend_head(qh, kh, vh, scale):
-    """One head: qh [Lq, D], kh [Lk, D], vh [Lk, D] (already rotated) -> [Lq, D]."""
-    s = (qh @ kh.T) * scale
-    m = s.max(axis=1, keepdims=True)
-    p = np.exp(s - m)
-    return (p @ vh) / p.sum(axis=1, keepdims=True)
+    """One head: qh [Lq, D], kh [Lk, D], vh [Lk, D] (already rotated) -> [Lq, D]:
+    the softmax weights of each row's scores, times the values."""
+    return softmax_rows((qh @ kh.T) * scale) @ vh
 
 
 def window_attention(q, q_t0, k, v, ctx_t0, grid_h, grid_w, pairs, base,

@@ -29,8 +29,8 @@ MAX_SEGMENTS = 8
 
 # Every entry point include/rfattn.h declares.
 EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
-           "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention", "rf_qkv_project",
-           "rf_set_frame_shift", "rf_add_frame_shift")
+           "rf_kvcache_bytes", "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention",
+           "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift")
 
 
 class RfError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
         L.rf_last_error.restype = ctypes.c_char_p
         L.rf_rope3d_apply.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp]
         L.rf_rope3d_apply.restype = i32
+        L.rf_kvcache_bytes.argtypes = [ctypes.POINTER(Geom), i32, ctypes.POINTER(i64)]
+        L.rf_kvcache_bytes.restype = i32
         L.rf_kvcache_roll.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, i64, i32, vp]
         L.rf_kvcache_roll.restype = i32
         L.rf_kvcache_plan_roll.argtypes = [ctypes.POINTER(KVCacheDesc), i64, i32,
@@ -145,12 +147,26 @@ def _destroy_pending():
         lib().rf_destroy(_pending_destroy.pop())
 
 
+def _geom(grid_h, grid_w, n_heads, head_dim, pairs, base, max_frame):
+    return Geom(grid_h, grid_w, n_heads, head_dim, (ctypes.c_int32 * 3)(*pairs), base, max_frame)
+
+
+def kvcache_bytes(capacity, grid_h=30, grid_w=52, n_heads=12, head_dim=128, pairs=(22, 21, 21),
+                  base=10000.0, max_frame=4096):
+    """Bytes of one ring buffer (K or V) of `capacity` slots (rf_kvcache_bytes, host-only);
+    raises RfError for an invalid geometry or a ring beyond the library's size limit."""
+    g = _geom(grid_h, grid_w, n_heads, head_dim, pairs, base, max_frame)
+    out = ctypes.c_int64()
+    _check(lib().rf_kvcache_bytes(ctypes.byref(g), capacity, ctypes.byref(out)))
+    return out.value
+
+
 class Context:
     """Geometry + device RoPE tables (rf_create / rf_destroy)."""
 
     def __init__(self, grid_h=30, grid_w=52, n_heads=12, head_dim=128, pairs=(22, 21, 21),
                  base=10000.0, max_frame=4096):
-        g = Geom(grid_h, grid_w, n_heads, head_dim, (ctypes.c_int32 * 3)(*pairs), base, max_frame)
+        g = _geom(grid_h, grid_w, n_heads, head_dim, pairs, base, max_frame)
         _destroy_pending()
         h = ctypes.c_void_p()
         _check(lib().rf_create(ctypes.byref(g), ctypes.byref(h)))
@@ -216,6 +232,8 @@ class KVCache:
 
     def __init__(self, ctx, capacity, device="cuda"):
         self.ctx = ctx
+        kvcache_bytes(capacity, ctx.grid_h, ctx.grid_w, ctx.n_heads, ctx.head_dim, ctx.pairs,
+                      ctx.base, ctx.max_frame)  # the size limit, before allocating
         shape_k = (capacity, ctx.n_heads, ctx.tokens_per_frame, ctx.head_dim)
         shape_v = (capacity, ctx.n_heads, ctx.head_dim, ctx.tokens_per_frame)
         self.k = torch.zeros(shape_k, dtype=torch.bfloat16, device=device)

@@ -111,6 +111,34 @@ rf_status check_ring(const rf_kvcache* c, bool need_memory) {
   return RF_OK;
 }
 
+// The attention kernel addresses a ring buffer (K or V) with 32-bit byte offsets
+// through one buffer resource and uses kRingOffsetLimit itself as its
+// "past the end, load zeros" offset, so every byte of a ring must lie below it.
+constexpr int64_t kRingOffsetLimit = 0x7FFFFFF0;
+
+// Bytes of one ring buffer (K or V) of `capacity` slots, or an error if the ring
+// cannot be addressed by the attention kernel.  Needs a validated geometry.
+rf_status ring_bytes(const rf_geom& g, int64_t capacity, int64_t* bytes) {
+  if (capacity < 1) return fail(RF_ERR_SHAPE, "cache capacity must be >= 1");
+  const int64_t slot = (int64_t)g.n_heads * g.grid_h * g.grid_w * g.head_dim * 2;
+  if (slot > kRingOffsetLimit / capacity || slot * capacity + 16 > kRingOffsetLimit)
+    return fail(RF_ERR_SHAPE,
+                "a ring of %lld slots of %lld bytes exceeds the attention kernel's 32-bit range "
+                "(at most %lld bytes per K or V buffer: capacity <= %lld)",
+                (long long)capacity, (long long)slot, (long long)(kRingOffsetLimit - 16),
+                (long long)((kRingOffsetLimit - 16) / slot));
+  *bytes = slot * capacity;
+  return RF_OK;
+}
+
+// check_ring plus the ring's byte size against the attention kernel's range.
+rf_status check_ring_geom(const rf_geom& g, const rf_kvcache* c, bool need_memory) {
+  rf_status st = check_ring(c, need_memory);
+  if (st != RF_OK) return st;
+  int64_t bytes = 0;
+  return ring_bytes(g, c->capacity, &bytes);
+}
+
 int64_t mod(int64_t a, int64_t m) {
   int64_t r = a % m;
   return r < 0 ? r + m : r;
@@ -197,6 +225,14 @@ void rf_destroy(rf_ctx* ctx) {
   delete ctx;
 }
 
+rf_status rf_kvcache_bytes(const rf_geom* g, int32_t capacity, int64_t* bytes) {
+  g_err[0] = 0;
+  rf_status st = check_geom(g);
+  if (st != RF_OK) return st;
+  if (!bytes) return fail(RF_ERR_NULL, "bytes is NULL");
+  return ring_bytes(*g, capacity, bytes);
+}
+
 rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* y, int64_t y_ld,
                           int64_t t0, int64_t n_tokens, void* stream) {
   g_err[0] = 0;
@@ -263,8 +299,8 @@ rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, i
   g_err[0] = 0;
   rf_status st = check_ctx(ctx);
   if (st != RF_OK) return st;
-  if ((st = check_ring(c, true)) != RF_OK) return st;
   const rf_geom& g = ctx->g;
+  if ((st = check_ring_geom(g, c, true)) != RF_OK) return st;
   const int64_t row = (int64_t)g.n_heads * g.head_dim;
   if ((st = check_tensor(k_new, k_ld, row, "k_new")) != RF_OK) return st;
   if ((st = check_tensor(v_new, v_ld, row, "v_new")) != RF_OK) return st;
@@ -306,8 +342,8 @@ rf_status rf_qkv_project(const rf_ctx* ctx, rf_kvcache* c, const void* x, int64_
   g_err[0] = 0;
   rf_status st = check_ctx(ctx);
   if (st != RF_OK) return st;
-  if ((st = check_ring(c, true)) != RF_OK) return st;
   const rf_geom& g = ctx->g;
+  if ((st = check_ring_geom(g, c, true)) != RF_OK) return st;
   const int64_t C = (int64_t)g.n_heads * g.head_dim;
   if ((st = check_tensor(x, x_ld, C, "x")) != RF_OK) return st;
   if ((st = check_tensor(w, w_ld, C, "w")) != RF_OK) return st;
@@ -388,7 +424,7 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   g_err[0] = 0;
   rf_status st = check_ctx(ctx);
   if (st != RF_OK) return st;
-  if ((st = check_ring(c, true)) != RF_OK) return st;
+  if ((st = check_ring_geom(ctx->g, c, true)) != RF_OK) return st;
   if (!segs) return fail(RF_ERR_NULL, "segments is NULL");
   if (n_segs < 1 || n_segs > RF_MAX_SEGMENTS)
     return fail(RF_ERR_SHAPE, "n_segs must be in 1..%d", RF_MAX_SEGMENTS);

@@ -145,3 +145,43 @@ def test_binding_rejects_host_and_wrong_typed_tensors():
         rf._check_shift(torch.zeros(1, dtype=torch.int64))
     with pytest.raises(TypeError):
         rf._check_shift(None)
+
+
+SLOT_30x52x12 = 12 * 30 * 52 * 128 * 2   # bytes of one ring slot at the workload geometry
+
+
+@pytest.mark.parametrize("capacity,ok", [(1, True), (21, True), (448, True), (449, False),
+                                         (897, False), (0, False), (-3, False)])
+def test_ring_size_limit_at_the_workload_geometry(L, capacity, ok):
+    """The attention kernel addresses a ring buffer with 32-bit offsets and uses
+    0x7FFFFFF0 as its past-the-end offset: 448 slots of 4,792,320 bytes fit, 449 do not
+    (that sentinel would fall inside the ring), 897 would wrap the offsets."""
+    if ok:
+        assert rf.kvcache_bytes(capacity) == capacity * SLOT_30x52x12
+        assert capacity * SLOT_30x52x12 + 16 <= 0x7FFFFFF0
+    else:
+        with pytest.raises(rf.RfError) as e:
+            rf.kvcache_bytes(capacity)
+        assert e.value.status == 3
+
+
+def test_ring_size_limit_with_a_large_slot(L):
+    """A legal geometry whose single slot already exceeds the 32-bit range (1024 x 1024
+    tokens per frame, 12 heads: 3.2 GB per slot) is refused at any capacity; a 1-head
+    slot of 256 MiB fits 7 times, not 8."""
+    with pytest.raises(rf.RfError) as e:
+        rf.kvcache_bytes(1, grid_h=1024, grid_w=1024)
+    assert e.value.status == 3
+    one_head = 1024 * 1024 * 128 * 2
+    assert rf.kvcache_bytes(7, grid_h=1024, grid_w=1024, n_heads=1) == 7 * one_head
+    with pytest.raises(rf.RfError):
+        rf.kvcache_bytes(8, grid_h=1024, grid_w=1024, n_heads=1)
+
+
+def test_ring_size_query_validates_its_arguments(L):
+    out = ctypes.c_int64(-1)
+    assert L.rf_kvcache_bytes(None, 21, ctypes.byref(out)) == 1
+    assert L.rf_kvcache_bytes(ctypes.byref(_geom()), 21, None) == 1
+    assert L.rf_kvcache_bytes(ctypes.byref(_geom(head_dim=64, pairs=(11, 11, 10))), 21,
+                              ctypes.byref(out)) == 3
+    assert out.value == -1  # untouched on error

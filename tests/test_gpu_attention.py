@@ -458,3 +458,33 @@ def test_attention_errors():
         rf.window_attention(small, cs, [rf.Segment(q[:2], 19, o[:2], 0, 3, q_tok0=N - 1)])
     assert e.value.status == 4
     torch.cuda.synchronize()
+
+
+def test_oversized_ring_is_refused_before_any_launch():
+    """A ring whose byte size reaches the attention kernel's 32-bit range (449 slots at
+    the workload geometry) is refused with RF_ERR_SHAPE by every call that takes a ring,
+    before anything is enqueued: the descriptor points at a small dummy buffer that no
+    kernel may touch, and the output canary stays intact."""
+    import ctypes
+    g = synth.FULL
+    ctx = _ctx(g)
+    N = g.tokens_per_frame
+    dummy = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    for capacity, count in ((449, 21), (897, 21)):
+        desc = rf.KVCacheDesc(dummy.data_ptr(), dummy.data_ptr(), capacity, count, 0)
+        q = torch.zeros((N, g.n_heads, g.head_dim), dtype=torch.bfloat16, device="cuda")
+        o = torch.full((N, g.n_heads, g.head_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+        seg = rf.SegmentDesc(q.data_ptr(), g.n_heads * g.head_dim, o.data_ptr(), g.n_heads * g.head_dim,
+                             20, 0, N, 0, 21, 0)
+        st = rf.lib().rf_window_attention(ctx.handle, ctypes.byref(desc), ctypes.byref(seg), 1, 0.0,
+                                          rf._stream(None))
+        assert st == 3, rf.lib().rf_last_error()
+        st = rf.lib().rf_kvcache_roll(ctx.handle, ctypes.byref(desc), q.data_ptr(), g.n_heads * g.head_dim,
+                                      q.data_ptr(), g.n_heads * g.head_dim, 20, 1, rf._stream(None))
+        assert st == 3, rf.lib().rf_last_error()
+        assert (desc.first, desc.count) == (0, count)
+        torch.cuda.synchronize()
+        assert bool((o == 7.0).all())
+    with pytest.raises(rf.RfError) as e:  # the binding refuses before allocating
+        rf.KVCache(ctx, 449)
+    assert e.value.status == 3

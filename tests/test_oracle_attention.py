@@ -29,6 +29,16 @@ def test_softmax_rows_sum_to_one():
     assert np.all(p >= 0)
 
 
+def test_attend_head_uses_the_normalised_weights():
+    """attend_head is the softmax weights (the pinned helper above) applied to V: with
+    V = I the output is the weight matrix itself, so its rows sum to 1."""
+    qh, kh = _rand((40, D), 4), _rand((D, D), 5)
+    o = attention.attend_head(qh, kh, np.eye(D), 1.0 / math.sqrt(D))
+    assert np.allclose(o.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(o >= 0)
+    assert np.allclose(o, attention.softmax_rows((qh @ kh.T) / math.sqrt(D)), rtol=0, atol=1e-15)
+
+
 def test_zero_query_gives_mean_of_values():
     q = np.zeros((3 * N, H, D))
     k = _rand((5 * N, H, D), 2)
