@@ -2,7 +2,9 @@
 split, against the float64 oracle (same tolerances as test_gpu_attention.py).
 
 * extreme softmax scales: 0.15 (logits with a standard deviation of ~2.5 in log2 units)
-  and 2^-10 (nearly uniform weights);
+  and 2^-10 (nearly uniform weights) against the tolerances; 0.25, where the bf16 operand
+  roundings alone exceed the max-abs bound, against the bound the bf16 precision model
+  (oracle/precision.py) derives on the same rows;
 * logits that start very negative and rise frame by frame (an offset of -20 log2 units at
   the first context frame up to 0 at the last), so the running row max, negative at first,
   rises by more than 8 several times as the kernel walks the context (the lazy rescale of
@@ -84,12 +86,53 @@ def _batched(cfg, scale=0.0, k_alpha=lambda t: 1.0, k_offset=lambda t: 0.0, q_of
     _check(data, qb, 5, ob, 0, 21, sample_rows(N, N, extra=24, seed=seed + 1), s, f"{cfg} B", rk)
 
 
-# Much larger logits amplify the bf16 rounding of the rotated inputs (which the float64
-# oracle does not have) to the size of the tolerance for any bf16 implementation: at
-# scale 0.25 a float64 emulation of bf16 operands alone already errs by 1.4e-2.
 @pytest.mark.parametrize("scale", [0.15, 2.0 ** -10])
 def test_extreme_scales(scale):
     _batched(31 if scale > 0.1 else 32, scale=scale, seed=5)
+
+
+def test_scale_one_quarter_within_the_bf16_precision_model():
+    """Softmax scale 0.25: here the bf16 operand roundings alone miss the absolute
+    tolerance (oracle/precision.py; tests/test_oracle_precision.py shows the model's own
+    max-abs error of 2.03e-2 on the cache-update rows), so the kernel is held to the
+    bound that model derives on the same rows instead.  The kernel rounds the scaled
+    rotated query and the keys exactly as the model does (the same bits), so what
+    separates the two is the rounding of the softmax weights against a different
+    reference maximum, the float32 sums and the final rounding: each at most a bf16 step
+    relative (2^-8), so ||kernel - model|| <= 2^-8 ||model||, and against the oracle the
+    kernel's max-abs, mean-abs and rel-L2 errors stay within 1.25x the model's (an
+    independent residual of relative size <= 2^-8 next to the model's ~6e-3 rel-L2 adds
+    at most a factor 1.2 in quadrature)."""
+    from oracle import precision
+    from gpu_util import errors
+    cfg, scale = 31, 0.25
+    ctx, cache, data = _ring(cfg)
+    qa = synth.frames(G, cfg, 0, 6, 15, synth.Q)
+    qb = synth.frame(G, cfg, 0, 5, synth.Q + synth.CLEAN)
+    oa = torch.empty((15 * N, G.n_heads, G.head_dim), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty((N, G.n_heads, G.head_dim), dtype=torch.bfloat16, device="cuda")
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), 6, oa, 0, 21), rf.Segment(up(qb), 5, ob, 0, 21)],
+                        scale=scale)
+    torch.cuda.synchronize()
+    k = np.concatenate([data[t][0] for t in range(21)])
+    v = np.concatenate([data[t][1] for t in range(21)])
+    rk = RotatedKeys(G)
+    geo = (G.grid_h, G.grid_w, G.pairs, G.base)
+    for what, q, q_t0, o, rows in (("A", qa, 6, oa, sample_rows(15 * N, N, extra=40, seed=5)),
+                                   ("B", qb, 5, ob, sample_rows(N, N, extra=24, seed=6))):
+        khs = [rk.get(t, data[t][2], data[t][0]) for t in range(21)]
+        want = oracle_rows(G, q, q_t0, khs, [data[t][1] for t in range(21)], rows, scale=scale)
+        model = precision.attend_rows(q, q_t0, k, v, 0, *geo, scale=scale, rows=rows)
+        got = f64(down(o))[rows]
+        assert np.all(np.isfinite(got))
+        m_max, m_mean, m_rel = errors(model, want)
+        g_max, g_mean, g_rel = errors(got, want)
+        d_rel = np.linalg.norm(got - model) / np.linalg.norm(model)
+        print(f"scale 0.25 {what}: model max={m_max:.4e} mean={m_mean:.3e} rel={m_rel:.3e}; "
+              f"kernel max={g_max:.4e} mean={g_mean:.3e} rel={g_rel:.3e}; kernel-model rel={d_rel:.3e}",
+              flush=True)
+        assert d_rel <= 2.0 ** -8, (what, d_rel)
+        assert g_max <= 1.25 * m_max and g_mean <= 1.25 * m_mean and g_rel <= 1.25 * m_rel, what
 
 
 def test_running_max_rises_from_very_negative_logits():
