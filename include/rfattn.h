@@ -274,6 +274,31 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c,
                               void* stream);
 
 /*
+ * rf_window_attention_noalloc -- rf_window_attention for callers that cannot
+ * allocate or free device memory once set up (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same validation,
+ * kernels and results (bit for bit), but the partial results of split query
+ * tiles go to a static device array of the library instead of the context's
+ * workspace.  No allocation happens in this call.
+ *
+ * The array holds the partial results of at most 256 split work-groups
+ * (2 x 256 x 130 KB = 68 MB; a launch splits over at most one work-group per
+ * compute unit, 256 on an MI355X).  Each device keeps its own copy from the
+ * library's load until the process ends; its address is looked up when the
+ * first context of a device is created.  A launch that would need more
+ * returns RF_ERR_SHAPE before anything is enqueued; RF_ERR_HIP if the array's
+ * address could not be looked up on ctx's device.  Nothing in it needs to
+ * start at zero (every partial result is written before it is read, inside the
+ * call's own launches).
+ * All noalloc calls on one device share the array, across contexts and
+ * streams: calls that overlap in time on one device race and give wrong
+ * results.  Order them (one stream, or synchronise).
+ */
+rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c,
+                                      const rf_attn_segment* segs, int32_t n_segs, float scale,
+                                      void* stream);
+
+/*
  * rf_set_frame_shift / rf_add_frame_shift -- replaying a captured steady-state
  * step.  A window step repeats with every frame index one higher than the
  * step before (the window slides by one frame; "Amazon and Reactor tune

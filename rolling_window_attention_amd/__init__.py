@@ -30,7 +30,8 @@ MAX_SEGMENTS = 8
 # Every entry point include/rfattn.h declares.
 EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
            "rf_kvcache_bytes", "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention",
-           "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift")
+           "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift",
+           "rf_window_attention_noalloc")
 
 
 class RfError(RuntimeError):
@@ -90,6 +91,8 @@ def lib():
         L.rf_window_attention.argtypes = [vp, ctypes.POINTER(KVCacheDesc),
                                           ctypes.POINTER(SegmentDesc), i32, ctypes.c_float, vp]
         L.rf_window_attention.restype = i32
+        L.rf_window_attention_noalloc.argtypes = L.rf_window_attention.argtypes
+        L.rf_window_attention_noalloc.restype = i32
         L.rf_qkv_project.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, vp, i64, i64, i32, vp]
         L.rf_qkv_project.restype = i32
         L.rf_set_frame_shift.argtypes = [vp, vp, i64]
@@ -301,6 +304,20 @@ class Segment:
 
 def window_attention(ctx, cache, segments, scale=0.0, stream=None):
     """All segments in one launch; outputs are written into each segment's o."""
+    _check(lib().rf_window_attention(ctx.handle, ctypes.byref(cache.desc), *_segments(ctx, segments),
+                                     scale, _stream(stream)))
+
+
+def window_attention_noalloc(ctx, cache, segments, scale=0.0, stream=None):
+    """window_attention with the library's static per-device scratch instead of the
+    context's workspace (rf_window_attention_noalloc): no allocation in the call; calls
+    that overlap in time on one device race."""
+    _check(lib().rf_window_attention_noalloc(ctx.handle, ctypes.byref(cache.desc), *_segments(ctx, segments),
+                                             scale, _stream(stream)))
+
+
+def _segments(ctx, segments):
+    """The rf_attn_segment array of a launch and its length."""
     if not 1 <= len(segments) <= MAX_SEGMENTS:
         raise ValueError(f"1..{MAX_SEGMENTS} segments per launch")
     arr = (SegmentDesc * len(segments))()
@@ -310,8 +327,7 @@ def window_attention(ctx, cache, segments, scale=0.0, stream=None):
         if nq != no:
             raise ValueError("q and o must hold the same number of tokens")
         arr[i] = SegmentDesc(qp, qld, op, old, s.q_t0, s.q_tok0, nq, s.ctx_t0, s.ctx_frames, 0)
-    _check(lib().rf_window_attention(ctx.handle, ctypes.byref(cache.desc), arr, len(segments),
-                                     scale, _stream(stream)))
+    return arr, len(segments)
 
 
 def plan_roll(capacity, first, count, t0, n_frames):

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -30,11 +31,47 @@ struct rf_ctx {
   float* d_partial;   // attention workspace: 2 * max_workers partial results
   const int64_t* d_shift;  // device frame shift added by every launch (NULL: none)
   int64_t max_shift;       // its clamp, validated against the tables
+  float* d_scratch;        // this device's static attention scratch (NULL if unavailable)
+  hipError_t scratch_err;  // why it is unavailable
 };
+
+// Static attention workspace for rf_window_attention_noalloc: room for the
+// partial results of kScratchWorkers split work-groups (two pieces each), 68 MB.
+// Each device holds its own copy from the library's load until the process
+// ends.  In host code `scratch` is only a host-side stand-in: its device
+// address comes from hipGetSymbolAddress, per device (scratch_address).
+constexpr int kScratchWorkers = 256;
+constexpr int64_t kScratchFloats = (int64_t)2 * kScratchWorkers * kPartFloats;
+static __device__ __align__(256) float scratch[kScratchFloats];
 
 namespace {
 
 thread_local char g_err[512] = "";
+
+// The device address of `scratch` on the current device, looked up once per
+// device (at its first rf_create) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+bool g_scratch_done[kMaxDevices] = {};
+
+float* scratch_address(int dev, hipError_t* err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? static_cast<float*>(ptr) : nullptr;
+    g_scratch_done[dev] = true;
+  }
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
 
 rf_status fail(rf_status s, const char* fmt, ...) {
   va_list ap;
@@ -208,6 +245,7 @@ rf_status rf_create(const rf_geom* g, rf_ctx** out) {
   c->d_partial = part;
   c->d_shift = nullptr;
   c->max_shift = 0;
+  c->d_scratch = scratch_address(dev, &c->scratch_err);  // its failure only disables the noalloc call
   c->tab.t = d;
   c->tab.h = d + off_h;
   c->tab.w = d + off_w;
@@ -419,9 +457,14 @@ rf_status rf_add_frame_shift(const rf_ctx* ctx, int64_t* d_shift, int64_t delta,
   return RF_OK;
 }
 
-rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs,
-                              int32_t n_segs, float scale, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Validation and launch arguments of one rf_window_attention call (everything but
+// the workspace pointer).  Enqueues nothing.
+rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs, int32_t n_segs,
+                          float scale, AttnArgs& a) {
   rf_status st = check_ctx(ctx);
   if (st != RF_OK) return st;
   if ((st = check_ring_geom(ctx->g, c, true)) != RF_OK) return st;
@@ -435,7 +478,6 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   const rf_geom& g = ctx->g;
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
   const int64_t row = (int64_t)g.n_heads * g.head_dim;
-  AttnArgs a;
   std::memset(&a, 0, sizeof(a));
   int64_t units = 0, tiles = 0;
   for (int i = 0; i < n_segs; ++i) {
@@ -487,7 +529,7 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   if (a.dp_tiles == tiles) sk_begin = units;
   a.sk_unit_begin = (uint32_t)sk_begin;
   a.n_workers = (int)std::min<int64_t>(slots, units - sk_begin);
-  a.partial = ctx->d_partial;
+  a.partial = nullptr;  // set by the caller
   a.n_segs = n_segs;
   a.k_ring = (const uint16_t*)c->k;
   a.v_ring = (const uint16_t*)c->v;
@@ -499,6 +541,41 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   a.c_log2 = scale * 1.4426950408889634f;
   a.tab = ctx->tab;
   a.fs = {ctx->d_shift, ctx->max_shift};
+  return RF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs,
+                              int32_t n_segs, float scale, void* stream) {
+  g_err[0] = 0;
+  AttnArgs a;
+  rf_status st = build_attn_args(ctx, c, segs, n_segs, scale, a);
+  if (st != RF_OK) return st;
+  a.partial = ctx->d_partial;
+  hipError_t e = launch_window_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  return RF_OK;
+}
+
+rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs,
+                                      int32_t n_segs, float scale, void* stream) {
+  g_err[0] = 0;
+  AttnArgs a;
+  rf_status st = build_attn_args(ctx, c, segs, n_segs, scale, a);
+  if (st != RF_OK) return st;
+  if (!ctx->d_scratch)
+    return fail(RF_ERR_HIP, "the static attention scratch of device %d is not available: %s", ctx->device,
+                hipGetErrorString(ctx->scratch_err));
+  const int64_t need = (int64_t)2 * a.n_workers * kPartFloats;
+  if (need > kScratchFloats)
+    return fail(RF_ERR_SHAPE,
+                "this launch needs %lld floats of attention scratch (%d split work-groups), the static "
+                "scratch holds %lld (%d work-groups)",
+                (long long)need, a.n_workers, (long long)kScratchFloats, kScratchWorkers);
+  a.partial = ctx->d_scratch;
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
   return RF_OK;
