@@ -299,6 +299,84 @@ rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c,
                                       void* stream);
 
 /*
+ * Device-resident ring descriptors, for steps replayed from a captured graph
+ * and for rolling several layers' rings in one launch.
+ *
+ * Source: every layer of the model reads and writes its own rolling KV cache,
+ * and the attention length changes from pass to pass while the window fills
+ * ("Amazon and Reactor tune Trainium for real-time video generation", section
+ * "Three problems for generic compilers"); a real-time step has a budget of
+ * tens of milliseconds for all layers ("Optimizing Real-Time Video Generation
+ * on Trainium Chips", section 3).
+ *
+ * An rf_kvcache_dev lives in device memory (caller-owned, 16-byte aligned, 32
+ * bytes) and describes one ring: its buffers and capacity, written only by
+ * rf_kvcache_upload, and its window (first, count), which the kernels of
+ * rf_kvcache_roll_layers advance on the device by the ring rule of
+ * rf_kvcache_roll (the frame shift included) and rf_window_attention_dev reads
+ * when its kernels run.  A graph that captured a step's launches therefore
+ * replays it with the window the device holds at replay time -- e.g. every
+ * step of a window that fills from empty, whose context grows frame by frame.
+ * The host-side rf_kvcache of the same ring (the "host descriptor") is still
+ * passed to every call: the host validates against it and advances it on
+ * success, as for rf_kvcache_roll; replays advance only the device copy.
+ * Callers keep the two describing the same buffers and capacity (write the
+ * device copy only with rf_kvcache_upload); the kernels clamp what they read
+ * (capacity to the host descriptor's, count to 1..capacity), so a stale device
+ * window gives wrong frames, never an access outside the ring.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t first;
+  int32_t count;
+  int32_t capacity;
+} rf_kvcache_dev;
+
+/*
+ * rf_kvcache_upload -- write n host descriptors (each validated as by
+ * rf_kvcache_roll: buffers, alignment, capacity, size limit) into the device
+ * array d_rings[0..n-1], on `stream` (a kernel: stream-ordered and capturable,
+ * no host-to-device copy).  1 <= n <= 65535.  Use it to create the device
+ * copies and to reset a window (upload a descriptor with count 0).
+ */
+rf_status rf_kvcache_upload(const rf_ctx* ctx, const rf_kvcache* rings, int32_t n,
+                            rf_kvcache_dev* d_rings, void* stream);
+
+/*
+ * rf_kvcache_roll_layers -- rf_kvcache_roll of the same frames t0..t0+n_frames-1
+ * into n_layers rings in ONE launch (grouped roll): layer l's keys and values
+ * are token-major at k_new + l*k_layer_stride and v_new + l*v_layer_stride
+ * (elements; strides >= 0, multiples of 8), its ring is d_rings[l], whose
+ * window the launch advances on the device.  rings[0..n_layers-1] are the host
+ * descriptors of the same rings: each is validated like rf_kvcache_roll's
+ * (the roll must be legal for every layer), and advanced on success.  Layers
+ * may have different capacities; they may not share a buffer.  Bit for bit the
+ * same ring contents as n_layers separate rf_kvcache_roll calls.
+ * 1 <= n_layers <= 65535.  Errors: those of rf_kvcache_roll, per layer.
+ */
+rf_status rf_kvcache_roll_layers(const rf_ctx* ctx, rf_kvcache* rings, rf_kvcache_dev* d_rings,
+                                 int32_t n_layers, const void* k_new, int64_t k_layer_stride,
+                                 int64_t k_ld, const void* v_new, int64_t v_layer_stride,
+                                 int64_t v_ld, int64_t t0, int32_t n_frames, void* stream);
+
+/*
+ * rf_window_attention_dev -- rf_window_attention over the window of a
+ * device-resident descriptor: every segment attends over all frames the ring
+ * holds when the kernels run (d_ring's first .. first+count-1), so a captured
+ * launch follows the window as it grows or slides.  Segments must give
+ * ctx_t0 == 0 and ctx_frames == 0; queries and outputs are as in
+ * rf_window_attention.  c is the ring's host descriptor (validated; the
+ * launch is checked as for a window of `capacity` frames).  Results equal an
+ * rf_window_attention call over the same frames up to float32 rounding (the
+ * key-split work may be cut differently).  Errors: those of
+ * rf_window_attention, RF_ERR_SHAPE for a segment with a context range.
+ */
+rf_status rf_window_attention_dev(const rf_ctx* ctx, const rf_kvcache* c,
+                                  const rf_kvcache_dev* d_ring, const rf_attn_segment* segs,
+                                  int32_t n_segs, float scale, void* stream);
+
+/*
  * rf_set_frame_shift / rf_add_frame_shift -- replaying a captured steady-state
  * step.  A window step repeats with every frame index one higher than the
  * step before (the window slides by one frame; "Amazon and Reactor tune

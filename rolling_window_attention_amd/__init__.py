@@ -31,7 +31,8 @@ MAX_SEGMENTS = 8
 EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_rope3d_apply",
            "rf_kvcache_bytes", "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention",
            "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift",
-           "rf_window_attention_noalloc")
+           "rf_window_attention_noalloc", "rf_kvcache_upload", "rf_kvcache_roll_layers",
+           "rf_window_attention_dev")
 
 
 class RfError(RuntimeError):
@@ -57,6 +58,13 @@ class SegmentDesc(ctypes.Structure):
                 ("o_ld", ctypes.c_int64), ("q_t0", ctypes.c_int64), ("q_tok0", ctypes.c_int32),
                 ("q_tokens", ctypes.c_int32), ("ctx_t0", ctypes.c_int64), ("ctx_frames", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class KVCacheDevDesc(ctypes.Structure):
+    """rf_kvcache_dev: the layout of a device-resident ring descriptor (DeviceRings keeps
+    them as rows of an int64 device tensor)."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("first", ctypes.c_int64),
+                ("count", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 _lib = None
@@ -93,6 +101,14 @@ def lib():
         L.rf_window_attention.restype = i32
         L.rf_window_attention_noalloc.argtypes = L.rf_window_attention.argtypes
         L.rf_window_attention_noalloc.restype = i32
+        L.rf_kvcache_upload.argtypes = [vp, ctypes.POINTER(KVCacheDesc), i32, vp, vp]
+        L.rf_kvcache_upload.restype = i32
+        L.rf_kvcache_roll_layers.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i32, vp, i64, i64, vp, i64,
+                                             i64, i64, i32, vp]
+        L.rf_kvcache_roll_layers.restype = i32
+        L.rf_window_attention_dev.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, ctypes.POINTER(SegmentDesc),
+                                              i32, ctypes.c_float, vp]
+        L.rf_window_attention_dev.restype = i32
         L.rf_qkv_project.argtypes = [vp, ctypes.POINTER(KVCacheDesc), vp, i64, vp, i64, vp, i64, i64, i32, vp]
         L.rf_qkv_project.restype = i32
         L.rf_set_frame_shift.argtypes = [vp, vp, i64]
@@ -336,3 +352,84 @@ def plan_roll(capacity, first, count, t0, n_frames):
     after = KVCacheDesc()
     _check(lib().rf_kvcache_plan_roll(ctypes.byref(d), t0, n_frames, ctypes.byref(after)))
     return after.first, after.count
+
+
+DEV_DESC_BYTES = ctypes.sizeof(KVCacheDevDesc)  # 32
+
+
+def _layered(t, name, n_heads, head_dim):
+    """Pointer, layer stride, row stride and tokens of a [layers, tokens, H, D] (or
+    [layers, tokens, H*D]) bf16 device tensor; a layer stride of 0 (expand) is allowed."""
+    if not isinstance(t, torch.Tensor) or t.dim() not in (3, 4):
+        raise ValueError(f"{name} must be [layers, tokens, H, D] or [layers, tokens, H*D]")
+    ptr, ld, tokens = _token_major(t[0], name, n_heads, head_dim)
+    return ptr, t.stride(0), ld, tokens
+
+
+class DeviceRings:
+    """Device-resident descriptors (rf_kvcache_dev) of the rings of `caches` -- KVCache
+    objects of one context, one per layer -- in one device array, written from the
+    caches' host descriptors by rf_kvcache_upload."""
+
+    def __init__(self, caches, stream=None):
+        self.caches = list(caches)
+        if not self.caches:
+            raise ValueError("at least one cache")
+        self.ctx = self.caches[0].ctx
+        if any(c.ctx is not self.ctx for c in self.caches):
+            raise ValueError("all caches must belong to one context")
+        self.buf = torch.zeros((len(self.caches), DEV_DESC_BYTES // 8), dtype=torch.int64,
+                               device=self.caches[0].k.device)
+        self._descs = (KVCacheDesc * len(self.caches))()
+        self.upload(stream)
+
+    def __len__(self):
+        return len(self.caches)
+
+    def ptr(self, layer=0):
+        if not 0 <= layer < len(self.caches):
+            raise IndexError(layer)
+        return ctypes.c_void_p(self.buf.data_ptr() + DEV_DESC_BYTES * layer)
+
+    def _gather(self):
+        for i, c in enumerate(self.caches):
+            self._descs[i] = c.desc
+
+    def _scatter(self):
+        for i, c in enumerate(self.caches):
+            c.desc.first, c.desc.count = self._descs[i].first, self._descs[i].count
+
+    def upload(self, stream=None):
+        """Write the caches' host descriptors to the device copies (rf_kvcache_upload)."""
+        self._gather()
+        _check(lib().rf_kvcache_upload(self.ctx.handle, self._descs, len(self.caches), self.ptr(0),
+                                       _stream(stream)))
+
+    def reset(self, stream=None):
+        """Empty every ring's window, on the host and (stream-ordered) on the device."""
+        for c in self.caches:
+            c.desc.first, c.desc.count = 0, 0
+        self.upload(stream)
+
+    def roll(self, k_new, v_new, t0, stream=None):
+        """Grouped roll (rf_kvcache_roll_layers): layer l's frames t0.. from k_new[l], v_new[l]
+        ([layers, n*N, H, D]) into ring l, one launch; windows advance on host and device."""
+        c = self.ctx
+        kp, ks, kld, nk = _layered(k_new, "k_new", c.n_heads, c.head_dim)
+        vp, vs, vld, nv = _layered(v_new, "v_new", c.n_heads, c.head_dim)
+        if k_new.shape[0] != len(self.caches) or v_new.shape[0] != len(self.caches):
+            raise ValueError("one input block per layer")
+        if nk != nv or nk % c.tokens_per_frame:
+            raise ValueError("k_new and v_new must hold the same whole number of frames")
+        self._gather()
+        _check(lib().rf_kvcache_roll_layers(c.handle, self._descs, self.ptr(0), len(self.caches), kp, ks, kld,
+                                            vp, vs, vld, t0, nk // c.tokens_per_frame, _stream(stream)))
+        self._scatter()
+
+
+def window_attention_dev(ctx, rings, layer, segments, scale=0.0, stream=None):
+    """rf_window_attention_dev: the segments (context fields 0) attend over the window of
+    ring `layer` of `rings` (a DeviceRings) as the device holds it when the kernels run."""
+    cache = rings.caches[layer]
+    _check(lib().rf_window_attention_dev(ctx.handle, ctypes.byref(cache.desc), rings.ptr(layer),
+                                         *_segments(ctx, segments), scale, _stream(stream)))

@@ -87,6 +87,7 @@ rf_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 24;  // device index math is exact below this
 constexpr int64_t kMaxProjLd = int64_t(1) << 22;  // 256 rows of the projection's operands: < 2^31 bytes
+constexpr int kMaxLayers = 65535;                 // rings per grouped roll (the grid's y extent)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -356,6 +357,9 @@ rf_status rf_kvcache_roll(const rf_ctx* ctx, rf_kvcache* c, const void* k_new, i
   a.v_new = (const uint16_t*)v_new;
   a.k_ld = k_ld;
   a.v_ld = v_ld;
+  a.k_layer_stride = a.v_layer_stride = 0;
+  a.rings = nullptr;
+  a.n_layers = 1;
   a.k_ring = (uint16_t*)c->k;
   a.v_ring = (uint16_t*)c->v;
   a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;
@@ -516,6 +520,7 @@ rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_
     if (units > (int64_t(1) << 31)) return fail(RF_ERR_SHAPE, "launch too large");
   }
   a.total_units = (uint32_t)units;
+  a.total_tiles = (int)tiles;
   // Whole rounds of tiles run one per work-group; the remainder is split.
   const int64_t slots = ctx->max_workers;
   a.dp_tiles = (int)(tiles / slots * slots);
@@ -576,6 +581,135 @@ rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c, co
                 "scratch holds %lld (%d work-groups)",
                 (long long)need, a.n_workers, (long long)kScratchFloats, kScratchWorkers);
   a.partial = ctx->d_scratch;
+  hipError_t e = launch_window_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  return RF_OK;
+}
+
+rf_status rf_kvcache_upload(const rf_ctx* ctx, const rf_kvcache* rings, int32_t n, rf_kvcache_dev* d_rings,
+                            void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if (!rings || !d_rings) return fail(RF_ERR_NULL, "rings / d_rings is NULL");
+  if (n < 1 || n > kMaxLayers) return fail(RF_ERR_SHAPE, "n must be in 1..%d", kMaxLayers);
+  if ((reinterpret_cast<uintptr_t>(d_rings) & 15u) != 0) return fail(RF_ERR_ALIGN, "d_rings is not 16-byte aligned");
+  for (int i = 0; i < n; ++i)
+    if ((st = check_ring_geom(ctx->g, &rings[i], true)) != RF_OK)
+      return fail(st, "ring %d: %s", i, std::string(g_err).c_str());
+  for (int i0 = 0; i0 < n; i0 += kUploadMax) {
+    UploadArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.n = std::min(kUploadMax, n - i0);
+    for (int i = 0; i < a.n; ++i) {
+      const rf_kvcache& r = rings[i0 + i];
+      a.d[i] = DevRing{(uint16_t*)r.k, (uint16_t*)r.v, r.first, r.count, r.capacity};
+    }
+    hipError_t e = launch_upload_rings(reinterpret_cast<DevRing*>(d_rings) + i0, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ring descriptor upload");
+  }
+  return RF_OK;
+}
+
+rf_status rf_kvcache_roll_layers(const rf_ctx* ctx, rf_kvcache* rings, rf_kvcache_dev* d_rings, int32_t n_layers,
+                                 const void* k_new, int64_t k_layer_stride, int64_t k_ld, const void* v_new,
+                                 int64_t v_layer_stride, int64_t v_ld, int64_t t0, int32_t n_frames, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if (!rings || !d_rings) return fail(RF_ERR_NULL, "rings / d_rings is NULL");
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(RF_ERR_SHAPE, "n_layers must be in 1..%d", kMaxLayers);
+  if ((reinterpret_cast<uintptr_t>(d_rings) & 15u) != 0) return fail(RF_ERR_ALIGN, "d_rings is not 16-byte aligned");
+  const rf_geom& g = ctx->g;
+  const int64_t row = (int64_t)g.n_heads * g.head_dim;
+  if ((st = check_tensor(k_new, k_ld, row, "k_new")) != RF_OK) return st;
+  if ((st = check_tensor(v_new, v_ld, row, "v_new")) != RF_OK) return st;
+  if (k_layer_stride < 0 || v_layer_stride < 0 || k_layer_stride % 8 != 0 || v_layer_stride % 8 != 0)
+    return fail(RF_ERR_ALIGN, "layer strides must be >= 0 and multiples of 8");
+  std::vector<rf_kvcache> after(n_layers);
+  std::vector<const void*> bufs;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_ring_geom(g, &rings[l], true)) != RF_OK) return fail(st, "layer %d: %s", l, std::string(g_err).c_str());
+    if ((st = rf_kvcache_plan_roll(&rings[l], t0, n_frames, &after[l])) != RF_OK)
+      return fail(st, "layer %d: %s", l, std::string(g_err).c_str());
+    bufs.push_back(rings[l].k);
+    bufs.push_back(rings[l].v);
+  }
+  std::sort(bufs.begin(), bufs.end());
+  if (std::adjacent_find(bufs.begin(), bufs.end()) != bufs.end())
+    return fail(RF_ERR_SHAPE, "two layers share a ring buffer");
+  if (t0 < 0 || t0 + n_frames + ctx->max_shift > g.max_frame)
+    return fail(RF_ERR_RANGE, "frames %lld..%lld outside the tables (max_frame %lld)", (long long)t0,
+                (long long)(t0 + n_frames - 1), (long long)g.max_frame);
+  const int64_t N = (int64_t)g.grid_h * g.grid_w;
+  if ((int64_t)n_frames * N >= kMaxTokens) return fail(RF_ERR_SHAPE, "too many tokens in one roll");
+  if ((int64_t)n_frames * g.n_heads > 65535) return fail(RF_ERR_SHAPE, "n_frames*n_heads must be <= 65535");
+
+  RollArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_ld = k_ld;
+  a.v_ld = v_ld;
+  a.k_layer_stride = k_layer_stride;
+  a.v_layer_stride = v_layer_stride;
+  a.rings = reinterpret_cast<DevRing*>(d_rings);
+  a.n_layers = n_layers;
+  a.slot_elems = (int64_t)g.n_heads * N * g.head_dim;
+  a.t0 = t0;
+  a.n_frames = n_frames;
+  a.W = rings[0].capacity;  // per layer from its descriptor on the device
+  a.N = (int)N;
+  a.gw = g.grid_w;
+  a.H = g.n_heads;
+  a.tab = ctx->tab;
+  a.fs = {ctx->d_shift, ctx->max_shift};
+  hipError_t e = launch_roll(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "grouped kvcache roll launch");
+  for (int l = 0; l < n_layers; ++l) {
+    rings[l].first = after[l].first;
+    rings[l].count = after[l].count;
+  }
+  return RF_OK;
+}
+
+rf_status rf_window_attention_dev(const rf_ctx* ctx, const rf_kvcache* c, const rf_kvcache_dev* d_ring,
+                                  const rf_attn_segment* segs, int32_t n_segs, float scale, void* stream) {
+  g_err[0] = 0;
+  rf_status st = check_ctx(ctx);
+  if (st != RF_OK) return st;
+  if ((st = check_ring_geom(ctx->g, c, true)) != RF_OK) return st;
+  if (!d_ring || !segs) return fail(RF_ERR_NULL, "d_ring / segments is NULL");
+  if ((reinterpret_cast<uintptr_t>(d_ring) & 15u) != 0) return fail(RF_ERR_ALIGN, "d_ring is not 16-byte aligned");
+  if (n_segs < 1 || n_segs > RF_MAX_SEGMENTS) return fail(RF_ERR_SHAPE, "n_segs must be in 1..%d", RF_MAX_SEGMENTS);
+  if (c->count == 0) return fail(RF_ERR_RANGE, "the cache holds no frames");
+  // Validate as a launch over the ring's largest window (capacity frames): the
+  // queries, the tables and the unit count; the window itself is read by the kernels.
+  std::vector<rf_attn_segment> full(segs, segs + n_segs);
+  rf_kvcache whole = *c;
+  whole.first = 0;
+  whole.count = c->capacity;
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].ctx_t0 != 0 || segs[i].ctx_frames != 0)
+      return fail(RF_ERR_SHAPE, "segment %d: ctx_t0 and ctx_frames must be 0 (the window is read on the device)", i);
+    full[i].ctx_t0 = 0;
+    full[i].ctx_frames = c->capacity;
+  }
+  AttnArgs a;
+  if ((st = build_attn_args(ctx, &whole, full.data(), n_segs, scale, a)) != RF_OK) return st;
+  // The split work-groups: as many as a launch over the host descriptor's window
+  // takes (so such a launch is cut the same way as rf_window_attention cuts it);
+  // with a smaller window at run time some of them get no work.
+  AttnArgs now;
+  for (int i = 0; i < n_segs; ++i) {
+    full[i].ctx_t0 = c->first;
+    full[i].ctx_frames = c->count;
+  }
+  if ((st = build_attn_args(ctx, c, full.data(), n_segs, scale, now)) != RF_OK) return st;
+  a.n_workers = now.n_workers;
+  if (a.dp_tiles < a.total_tiles && a.n_workers < 1) a.n_workers = 1;
+  a.ring_dev = reinterpret_cast<const DevRing*>(d_ring);
+  a.partial = ctx->d_partial;
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
   return RF_OK;

@@ -31,6 +31,23 @@ __device__ __forceinline__ int64_t frame_shift(const FrameShift& s) {
   return v < 0 ? 0 : (v > s.max ? s.max : v);
 }
 
+// A ring descriptor in device memory (rf_kvcache_dev of the C ABI): the
+// buffers and capacity are written by the upload kernel only, the window
+// (first, count) also by the rolls that use the descriptor.
+struct DevRing {
+  uint16_t* k;       // [W][H][N][D]
+  uint16_t* v;       // [W][H][D][N]
+  int64_t first;
+  int32_t count;
+  int32_t capacity;  // W
+};
+static_assert(sizeof(DevRing) == 32, "rf_kvcache_dev layout");
+
+__device__ __forceinline__ int64_t mod_pos(int64_t a, int64_t m) {
+  const int64_t r = a % m;
+  return r < 0 ? r + m : r;
+}
+
 struct RopeArgs {
   const uint16_t* x;
   uint16_t* y;
@@ -45,12 +62,15 @@ struct RollArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t k_ld, v_ld;
+  int64_t k_layer_stride, v_layer_stride;  // elements between layers' inputs (grid.y = layer)
+  DevRing* rings;        // per-layer device descriptors (NULL: the one ring below)
   uint16_t* k_ring;      // [W][H][N][D]
   uint16_t* v_ring;      // [W][H][D][N]
   int64_t slot_elems;    // H*N*D
   int64_t t0;            // first new frame
   int slot0;             // t0 % W
   int n_frames, W, N, gw, H;
+  int n_layers;          // rings written by one launch (grid.y); 1 without descriptors
   RopeTables tab;
   FrameShift fs;
 };
@@ -74,6 +94,7 @@ struct AttnArgs {
   SegDev seg[kMaxSegments];
   int n_segs;
   uint32_t total_units;  // sum over segments of heads * q_tiles * key_tiles
+  int total_tiles;       // sum over segments of heads * q_tiles
   int dp_tiles;          // tiles run whole, one work-group each (full rounds)
   uint32_t sk_unit_begin;  // first unit of the split tiles (= unit of tile dp_tiles)
   int n_workers;         // work-groups sharing the split tiles' units (0: none)
@@ -83,6 +104,11 @@ struct AttnArgs {
   int W, N, gw, H;
   float c_log2;          // scale * log2(e)
   float* partial;        // workspace: 2 * n_workers partial results of kPartFloats
+  // Window mode (non-NULL): the ring's buffers and window come from this device
+  // descriptor when the kernels run, and every segment attends over the whole
+  // window; per-segment context fields and unit counts are then derived on the
+  // device (key tiles per query tile = window keys / kAttnBlockN, the same for all).
+  const DevRing* ring_dev;
   RopeTables tab;
   FrameShift fs;
 };
@@ -114,5 +140,12 @@ hipError_t prepare_window_attn();  // once per device, before the first launch
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
 hipError_t prepare_qkv_proj();     // once per device, before the first launch
 hipError_t launch_add_shift(int64_t* p, int64_t delta, hipStream_t s);
+// Write n <= kUploadMax descriptors into device memory (a kernel: stream-ordered, capturable).
+constexpr int kUploadMax = 32;
+struct UploadArgs {
+  DevRing d[kUploadMax];
+  int n;
+};
+hipError_t launch_upload_rings(DevRing* dst, const UploadArgs& a, hipStream_t s);
 
 }  // namespace rfattn

@@ -122,12 +122,44 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 constexpr int kVBlock = 128;  // tokens per value work-group (multiple of 8)
 static_assert(kVBlock % 8 == 0, "value block");
 
+// The window a roll of frames t0..t0+n-1 leaves (the host's ring rule, applied on
+// the device to a device-resident descriptor): overwrite inside the window,
+// append after it, evict the oldest frames beyond the capacity.
+__device__ void advance_window(DevRing* r, int64_t t0, int n) {
+  const int W = r->capacity > 0 ? r->capacity : 1;
+  int64_t first = r->first;
+  int64_t end = first + (r->count > 0 ? r->count : 0);
+  if (r->count <= 0) first = end = t0;
+  const int64_t new_end = end > t0 + n ? end : t0 + n;
+  int64_t count = new_end - first;
+  if (count > W) {
+    first = new_end - W;
+    count = W;
+  }
+  r->first = first;
+  r->count = (int32_t)count;
+}
+
 // Work-groups [0, v_blocks): value blocks as above.  Work-groups from v_blocks
 // on: keys of tokens [tok_base, tok_base + k_tokens), a thread per (token, head
 // group, 16-byte column) as in rope3d, rotated and stored to K[slot][h][n][d].
 // The longer value work-groups come first so that they do not form a tail.
+// blockIdx.y is the layer: its inputs sit layer_stride elements further, its
+// ring is a.rings[layer] when per-layer device descriptors are given (whose
+// window the layer's first work-group advances when `advance` is set).
 __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks, uint32_t tok_base,
-                                                   uint32_t k_tokens) {
+                                                   uint32_t k_tokens, int advance) {
+  const int64_t sh = frame_shift(a.fs);
+  if (a.rings) {
+    DevRing* r = a.rings + blockIdx.y;
+    a.k_ring = r->k;
+    a.v_ring = r->v;
+    a.W = r->capacity > 0 ? r->capacity : 1;
+    a.slot0 = (int)mod_pos(a.t0, a.W);
+    a.k_new += (int64_t)blockIdx.y * a.k_layer_stride;
+    a.v_new += (int64_t)blockIdx.y * a.v_layer_stride;
+    if (advance && blockIdx.x == 0 && threadIdx.x == 0) advance_window(r, a.t0 + sh, a.n_frames);
+  }
   if (blockIdx.x >= v_blocks) {
     uint32_t tl;
     int h0;
@@ -136,7 +168,6 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks
     if (tl >= k_tokens) return;
     const uint32_t tok = tok_base + tl;
     const TokPos p = tok_pos(tok, (uint32_t)a.N, 1.0f / (float)a.N, (uint32_t)a.gw, 1.0f / (float)a.gw);
-    const int64_t sh = frame_shift(a.fs);
     int slot = a.slot0 + (int)(sh % a.W);
     if (slot >= a.W) slot -= a.W;
     slot += (int)p.f;
@@ -158,7 +189,7 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks
   const uint32_t fh = fhd >> 1, dh = fhd & 1u;
   const int f = (int)fh / a.H;
   const int h = (int)fh - f * a.H;
-  int slot = a.slot0 + (int)(frame_shift(a.fs) % a.W);
+  int slot = a.slot0 + (int)(sh % a.W);
   if (slot >= a.W) slot -= a.W;
   slot += f;
   if (slot >= a.W) slot -= a.W;
@@ -210,11 +241,21 @@ hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
     const uint64_t rows = (uint64_t)n * (uint64_t)((a.H + kRopeHpt - 1) / kRopeHpt);
     const uint32_t k_blocks = (uint32_t)((rows + kRopeRows - 1) / kRopeRows);
     const uint32_t vb = t == 0 ? v_blocks : 0u;  // value blocks ride with the first piece
-    hipLaunchKernelGGL(roll_kernel, dim3(vb + k_blocks), dim3(256), 0, s, a, vb, t, n);
+    hipLaunchKernelGGL(roll_kernel, dim3(vb + k_blocks, (unsigned)a.n_layers), dim3(256), 0, s, a, vb, t, n,
+                       t == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+__global__ void upload_rings_kernel(DevRing* dst, UploadArgs a) {
+  if ((int)threadIdx.x < a.n) dst[threadIdx.x] = a.d[threadIdx.x];
+}
+
+hipError_t launch_upload_rings(DevRing* dst, const UploadArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(upload_rings_kernel, dim3(1), dim3(kUploadMax), 0, s, dst, a);
+  return hipGetLastError();
 }
 
 // *p += delta on the stream (a one-thread kernel: stream-ordered and capturable).

@@ -181,11 +181,22 @@ __device__ __forceinline__ void mfma_o<3>(bf16x8 a, u32x4 b) {
                : "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63");
 }
 
-// One work item: query tile qt of head h of segment sg, key tiles [ka, kb).
-// A complete item (all key tiles) writes the normalised bf16 output; a piece
-// of a split tile writes its partial result to `part`.
+// The context a work item attends over: the ring's buffers and capacity, the
+// slot of its first frame (frame shift included) and its keys.
+struct CtxView {
+  const uint16_t* k_ring;
+  const uint16_t* v_ring;
+  int W;
+  int ctx_slot0;
+  int ctx_keys;
+  int key_tiles;
+};
+
+// One work item: query tile qt of head h of segment sg over context cv, key
+// tiles [ka, kb).  A complete item (all key tiles) writes the normalised bf16
+// output; a piece of a split tile writes its partial result to `part`.
 template <bool kSmallN>
-__device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const SegDev& sg,
+__device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const SegDev& sg, const CtxView& cv,
                                          int h, int qt, int ka, int kb, float* part) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -222,16 +233,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   // The K pipeline runs one tile ahead of the V pipeline: tile j's keys are
   // needed in iteration j (scores), its values in iteration j+1 (after the
   // softmax), so two LDS buffers per operand suffice.
-  const int nkeys = sg.ctx_keys;
+  const int nkeys = cv.ctx_keys;
   const int ntiles = kb - ka;  // key tiles of this item: ka .. kb-1
   const int N = a.N;
-  const int W = a.W;
+  const int W = cv.W;
   const uint32_t slot_b = (uint32_t)a.slot_elems * 2u;
   const uint32_t ring_b = slot_b * (uint32_t)W;
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_ring), 0, (int)ring_b, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(cv.k_ring), 0, (int)ring_b, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_ring), 0, (int)ring_b, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(cv.v_ring), 0, (int)ring_b, kBufferWord3);
   const uint32_t k_head = (uint32_t)h * (uint32_t)N * (kHeadDim * 2u);  // K: [H][N][D]
   const uint32_t v_head = (uint32_t)h * kHeadDim * (uint32_t)N * 2u;    // V: [H][D][N]
   // K: rows (tid>>4) + 32i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 64i, key chunk tid&7.
@@ -250,7 +261,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     const int key0 = ka * kBlockN;
     const int f0 = key0 / N;
     kn = key0 - f0 * N;
-    kslot = (sg.ctx_slot0 + (int)(frame_shift(a.fs) % W) + f0) % W;
+    kslot = (cv.ctx_slot0 + f0) % W;
   }
   int kload = ka;
   int vslot = kslot, vn = kn, vload = ka;
@@ -555,7 +566,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
 
   // ---- epilogue --------------------------------------------------------------------
   const float l_tot = xhalf_sum(l_run);
-  if (ka == 0 && kb == sg.key_tiles) {  // whole item: O = O^T / l, bf16, token-major
+  if (ka == 0 && kb == cv.key_tiles) {  // whole item: O = O^T / l, bf16, token-major
     const float inv = 1.0f / l_tot;
     if (qvalid) {
       uint16_t* orow = sg.o + (int64_t)qi * sg.o_ld + h * kHeadDim;
@@ -594,13 +605,52 @@ __device__ __forceinline__ uint32_t range_start(uint32_t v, uint32_t U, uint32_t
   return (uint32_t)(((uint64_t)v * U) / P);
 }
 
-// Segment, query tile and key tile of unit u.
-__device__ __forceinline__ int unit_segment(const AttnArgs& a, uint32_t u) {
+// How a launch's work units (query tile x key tile) are numbered.  With host
+// context ranges the counts come with the arguments; in window mode every
+// segment has the window's key tiles, so a segment's first unit is its first
+// tile times that count.
+struct Units {
+  uint32_t total;     // all units of the launch
+  uint32_t sk_begin;  // first unit of the split tiles
+  uint32_t kt;        // window mode: key tiles per query tile (0: per segment)
+};
+
+// The launch's context in window mode: the ring descriptor as the device holds it
+// now (capacity clamped to the validated one, at least one frame of the window).
+__device__ __forceinline__ CtxView window_view(const AttnArgs& a) {
+  const DevRing* r = a.ring_dev;
+  const int cap = r->capacity;
+  const int W = cap < 1 ? 1 : (cap > a.W ? a.W : cap);
+  const int cnt = r->count < 1 ? 1 : (r->count > W ? W : r->count);
+  const int keys = cnt * a.N;
+  return CtxView{r->k, r->v, W, (int)mod_pos(r->first, W), keys, (keys + kBlockN - 1) / kBlockN};
+}
+
+__device__ __forceinline__ Units launch_units(const AttnArgs& a, const CtxView& wv) {
+  if (!a.ring_dev) return Units{a.total_units, a.sk_unit_begin, 0u};
+  const uint32_t kt = (uint32_t)wv.key_tiles;
+  return Units{(uint32_t)a.total_tiles * kt, (uint32_t)a.dp_tiles * kt, kt};
+}
+
+__device__ __forceinline__ uint32_t seg_unit_begin(const AttnArgs& a, const Units& un, int s) {
+  return un.kt ? (uint32_t)a.seg[s].tile_begin * un.kt : a.seg[s].unit_begin;
+}
+
+// Segment of unit u.
+__device__ __forceinline__ int unit_segment(const AttnArgs& a, const Units& un, uint32_t u) {
   int si = 0;
 #pragma unroll
   for (int s = 1; s < kMaxSegments; ++s)
-    if (s < a.n_segs && u >= a.seg[s].unit_begin) si = s;
+    if (s < a.n_segs && u >= seg_unit_begin(a, un, s)) si = s;
   return si;
+}
+
+// The context of segment sg: the window (window mode) or its own range.
+__device__ __forceinline__ CtxView seg_view(const AttnArgs& a, const SegDev& sg, const CtxView& wv) {
+  if (a.ring_dev) return wv;
+  const int W = a.W;
+  return CtxView{a.k_ring, a.v_ring, W, (sg.ctx_slot0 + (int)(frame_shift(a.fs) % W)) % W, sg.ctx_keys,
+                 sg.key_tiles};
 }
 
 // kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
@@ -609,6 +659,8 @@ __device__ __forceinline__ int unit_segment(const AttnArgs& a, uint32_t u) {
 template <bool kSmallN>
 __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  CtxView wv{};
+  if (a.ring_dev) wv = window_view(a);
   if ((int)blockIdx.x < a.dp_tiles) {
     // whole query tiles, one per work-group, in XCD-contiguous order
     const int tile = xcd_tile(blockIdx.x, a.dp_tiles);
@@ -618,29 +670,32 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
     for (int s = 1; s < kMaxSegments; ++s)
       if (s < a.n_segs && u >= (uint32_t)a.seg[s].tile_begin) si = s;
     const SegDev& sg = a.seg[si];
+    const CtxView cv = seg_view(a, sg, wv);
     const int tl = tile - sg.tile_begin;
     const int h = tl / sg.q_tiles;
-    run_item<kSmallN>(a, lds, sg, h, tl - h * sg.q_tiles, 0, sg.key_tiles, nullptr);
+    run_item<kSmallN>(a, lds, sg, cv, h, tl - h * sg.q_tiles, 0, cv.key_tiles, nullptr);
     return;
   }
   // the remaining tiles: equal contiguous ranges of key-tile units per worker
+  const Units un = launch_units(a, wv);
   const uint32_t P = (uint32_t)a.n_workers;
   const uint32_t v = (uint32_t)xcd_tile(blockIdx.x - a.dp_tiles, a.n_workers);
-  const uint32_t span = a.total_units - a.sk_unit_begin;
-  const uint32_t r0 = a.sk_unit_begin + range_start(v, span, P);
-  const uint32_t r1 = a.sk_unit_begin + range_start(v + 1, span, P);
+  const uint32_t span = un.total - un.sk_begin;
+  const uint32_t r0 = un.sk_begin + range_start(v, span, P);
+  const uint32_t r1 = un.sk_begin + range_start(v + 1, span, P);
   for (uint32_t u = r0; u < r1;) {
-    const int si = unit_segment(a, u);
+    const int si = unit_segment(a, un, u);
     const SegDev& sg = a.seg[si];
-    const uint32_t local = u - sg.unit_begin;
-    const int tl = (int)(local / (uint32_t)sg.key_tiles);
-    const int ka = (int)local - tl * sg.key_tiles;
-    const int kb = (int)min((uint32_t)sg.key_tiles, (uint32_t)ka + (r1 - u));
+    const CtxView cv = seg_view(a, sg, wv);
+    const uint32_t local = u - seg_unit_begin(a, un, si);
+    const int tl = (int)(local / (uint32_t)cv.key_tiles);
+    const int ka = (int)local - tl * cv.key_tiles;
+    const int kb = (int)min((uint32_t)cv.key_tiles, (uint32_t)ka + (r1 - u));
     const int h = tl / sg.q_tiles;
     const int qt = tl - h * sg.q_tiles;
     float* part = a.partial + (size_t)(2 * v + (u == r0 ? 0 : 1)) * kPartFloats;
     __syncthreads();  // the previous item's LDS reads are done
-    run_item<kSmallN>(a, lds, sg, h, qt, ka, kb, part);
+    run_item<kSmallN>(a, lds, sg, cv, h, qt, ka, kb, part);
     u += (uint32_t)(kb - ka);
   }
 }
@@ -655,25 +710,34 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
 __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
   constexpr int kChunks = kHeadDim / 8;
   __shared__ __attribute__((aligned(16))) uint16_t img[kPartRows * kHeadDim];
+  CtxView wv{};
+  if (a.ring_dev) wv = window_view(a);
+  const Units un = launch_units(a, wv);
   const uint32_t P = (uint32_t)a.n_workers;
-  const uint32_t span = a.total_units - a.sk_unit_begin;
+  const uint32_t span = un.total - un.sk_begin;
   const uint32_t v = blockIdx.x;
-  const uint32_t r0 = a.sk_unit_begin + range_start(v, span, P);
-  const uint32_t r1 = a.sk_unit_begin + range_start(v + 1, span, P);
+  const uint32_t r0 = un.sk_begin + range_start(v, span, P);
+  const uint32_t r1 = un.sk_begin + range_start(v + 1, span, P);
+  if (r1 <= r0) return;  // an empty range (not produced by the host's worker count)
   const uint32_t last = r1 - 1;
-  const int si = unit_segment(a, last);
+  const int si = unit_segment(a, un, last);
   const SegDev& sg = a.seg[si];
-  const uint32_t tl = (last - sg.unit_begin) / (uint32_t)sg.key_tiles;
-  const uint32_t t0 = sg.unit_begin + tl * (uint32_t)sg.key_tiles;  // the tile's units [t0, t1)
-  const uint32_t t1 = t0 + (uint32_t)sg.key_tiles;
+  const uint32_t kt = (uint32_t)seg_view(a, sg, wv).key_tiles;
+  const uint32_t ub = seg_unit_begin(a, un, si);
+  const uint32_t tl = (last - ub) / kt;
+  const uint32_t t0 = ub + tl * kt;  // the tile's units [t0, t1)
+  const uint32_t t1 = t0 + kt;
   if (t0 < r0 || t1 <= r1) return;  // started in an earlier range, or not split
   const int h = (int)tl / sg.q_tiles;
   const int qt = (int)tl - h * sg.q_tiles;
   const int r = threadIdx.x >> 1;  // row inside the query tile
   const int jh = threadIdx.x & 1;  // which four of each chunk's eight dims
 
+  // Workers with an empty range wrote no piece (window mode: the worker count was
+  // fixed for the window at the call, the window at run time may be smaller).
   float M = -INFINITY;
-  for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
+  for (uint32_t w = v; w < P && un.sk_begin + range_start(w, span, P) < t1; ++w) {
+    if (range_start(w + 1, span, P) == range_start(w, span, P)) continue;
     const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
     M = fmaxf(M, p[kPartRows * kHeadDim + r]);
   }
@@ -681,7 +745,8 @@ __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
-  for (uint32_t w = v; w < P && a.sk_unit_begin + range_start(w, span, P) < t1; ++w) {
+  for (uint32_t w = v; w < P && un.sk_begin + range_start(w, span, P) < t1; ++w) {
+    if (range_start(w + 1, span, P) == range_start(w, span, P)) continue;
     const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
     const float sc = __builtin_amdgcn_exp2f(p[kPartRows * kHeadDim + r] - M);
     L += sc * p[kPartRows * kHeadDim + kPartRows + r];

@@ -115,7 +115,8 @@ def test_plan_roll_rejects_bad_descriptors(L):
 def test_binding_structs_match_the_header(tmp_path):
     """The ctypes structures have the C structures' sizes and field offsets (the header
     compiled by the host C compiler)."""
-    pairs = [(rf.Geom, "rf_geom"), (rf.KVCacheDesc, "rf_kvcache"), (rf.SegmentDesc, "rf_attn_segment")]
+    pairs = [(rf.Geom, "rf_geom"), (rf.KVCacheDesc, "rf_kvcache"), (rf.SegmentDesc, "rf_attn_segment"),
+             (rf.KVCacheDevDesc, "rf_kvcache_dev")]
     lines = ["#include <stddef.h>", "#include <stdio.h>", f'#include "{HEADER}"', "int main(void) {"]
     for cls, cname in pairs:
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
