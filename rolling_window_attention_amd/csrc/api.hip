@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -465,6 +466,24 @@ rf_status rf_add_frame_shift(const rf_ctx* ctx, int64_t* d_shift, int64_t delta,
 
 namespace {
 
+// Pieces per split tile: the tiles of the last, partial round (tail < slots of
+// them) are each cut into n equal key ranges, one work-group per piece, merged
+// afterwards.  Choose the n that ends those rounds soonest -- ceil(n*tail/slots)
+// rounds of 1/n of a tile -- with every piece at least one key tile and all
+// partial results in the workspace (max_pieces); ties go to the smaller n.
+int choose_split(int64_t tail, int64_t slots, int64_t min_key_tiles, int64_t max_pieces) {
+  int best = 1;
+  double best_t = 1.0;  // one round of whole tiles
+  for (int64_t n = 2; tail > 0 && n <= min_key_tiles && n * tail <= max_pieces; ++n) {
+    const double t = (double)((n * tail + slots - 1) / slots) / (double)n;
+    if (t < best_t - 1e-9) {
+      best = (int)n;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 // Validation and launch arguments of one rf_window_attention call (everything but
 // the workspace pointer).  Enqueues nothing.
 rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs, int32_t n_segs,
@@ -483,7 +502,7 @@ rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_
   const int64_t N = (int64_t)g.grid_h * g.grid_w;
   const int64_t row = (int64_t)g.n_heads * g.head_dim;
   std::memset(&a, 0, sizeof(a));
-  int64_t units = 0, tiles = 0;
+  int64_t units = 0, tiles = 0, min_key_tiles = INT64_MAX;
   for (int i = 0; i < n_segs; ++i) {
     const rf_attn_segment& s = segs[i];
     if ((st = check_tensor(s.q, s.q_ld, row, "q")) != RF_OK) return st;
@@ -514,26 +533,18 @@ rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_
     d.ctx_slot0 = (int)mod(s.ctx_t0, c->capacity);
     d.key_tiles = (d.ctx_keys + kAttnBlockN - 1) / kAttnBlockN;
     d.tile_begin = (int)tiles;
-    d.unit_begin = (uint32_t)units;
     tiles += (int64_t)d.q_tiles * g.n_heads;
     units += (int64_t)d.q_tiles * g.n_heads * d.key_tiles;
+    min_key_tiles = std::min<int64_t>(min_key_tiles, d.key_tiles);
     if (units > (int64_t(1) << 31)) return fail(RF_ERR_SHAPE, "launch too large");
   }
-  a.total_units = (uint32_t)units;
   a.total_tiles = (int)tiles;
-  // Whole rounds of tiles run one per work-group; the remainder is split.
+  // Whole rounds of tiles run one per work-group; the tiles of the last, partial
+  // round are cut into equal key ranges.
   const int64_t slots = ctx->max_workers;
   a.dp_tiles = (int)(tiles / slots * slots);
-  int64_t sk_begin = 0;
-  for (int i = 0; i < n_segs; ++i) {  // unit index of tile dp_tiles
-    const SegDev& d = a.seg[i];
-    const int64_t seg_tiles = (int64_t)d.q_tiles * g.n_heads;
-    if (a.dp_tiles >= d.tile_begin && a.dp_tiles < d.tile_begin + seg_tiles)
-      sk_begin = d.unit_begin + (int64_t)(a.dp_tiles - d.tile_begin) * d.key_tiles;
-  }
-  if (a.dp_tiles == tiles) sk_begin = units;
-  a.sk_unit_begin = (uint32_t)sk_begin;
-  a.n_workers = (int)std::min<int64_t>(slots, units - sk_begin);
+  a.split_tiles = (int)(tiles - a.dp_tiles);
+  a.n_split = choose_split(a.split_tiles, slots, min_key_tiles, 2 * slots);
   a.partial = nullptr;  // set by the caller
   a.n_segs = n_segs;
   a.k_ring = (const uint16_t*)c->k;
@@ -574,12 +585,12 @@ rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c, co
   if (!ctx->d_scratch)
     return fail(RF_ERR_HIP, "the static attention scratch of device %d is not available: %s", ctx->device,
                 hipGetErrorString(ctx->scratch_err));
-  const int64_t need = (int64_t)2 * a.n_workers * kPartFloats;
-  if (need > kScratchFloats)
+  const int64_t need = (int64_t)a.split_tiles * a.n_split * kPartFloats;
+  if (a.n_split > 1 && need > kScratchFloats)
     return fail(RF_ERR_SHAPE,
-                "this launch needs %lld floats of attention scratch (%d split work-groups), the static "
-                "scratch holds %lld (%d work-groups)",
-                (long long)need, a.n_workers, (long long)kScratchFloats, kScratchWorkers);
+                "this launch needs %lld floats of attention scratch (%d partial results), the static "
+                "scratch holds %lld (%d)",
+                (long long)need, a.split_tiles * a.n_split, (long long)kScratchFloats, 2 * kScratchWorkers);
   a.partial = ctx->d_scratch;
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
@@ -697,17 +708,16 @@ rf_status rf_window_attention_dev(const rf_ctx* ctx, const rf_kvcache* c, const 
   }
   AttnArgs a;
   if ((st = build_attn_args(ctx, &whole, full.data(), n_segs, scale, a)) != RF_OK) return st;
-  // The split work-groups: as many as a launch over the host descriptor's window
-  // takes (so such a launch is cut the same way as rf_window_attention cuts it);
-  // with a smaller window at run time some of them get no work.
+  // The split tiles are cut as a launch over the host descriptor's window would be
+  // (so that such a launch gives the bits of rf_window_attention over the same
+  // frames); with fewer key tiles at run time than pieces, some pieces are empty.
   AttnArgs now;
   for (int i = 0; i < n_segs; ++i) {
     full[i].ctx_t0 = c->first;
     full[i].ctx_frames = c->count;
   }
   if ((st = build_attn_args(ctx, c, full.data(), n_segs, scale, now)) != RF_OK) return st;
-  a.n_workers = now.n_workers;
-  if (a.dp_tiles < a.total_tiles && a.n_workers < 1) a.n_workers = 1;
+  a.n_split = now.n_split;
   a.ring_dev = reinterpret_cast<const DevRing*>(d_ring);
   a.partial = ctx->d_partial;
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);

@@ -85,29 +85,26 @@ struct SegDev {
   int q_tiles;           // ceil(q_tokens / kAttnBlockM)
   int ctx_keys;          // ctx_frames * N
   int ctx_slot0;         // ring slot of the first context frame
-  int key_tiles;         // ceil(ctx_keys / kAttnBlockN): work units per query tile
+  int key_tiles;         // ceil(ctx_keys / kAttnBlockN)
   int tile_begin;        // first query tile of this segment (over all segments)
-  uint32_t unit_begin;   // first work unit of this segment
 };
 
 struct AttnArgs {
   SegDev seg[kMaxSegments];
   int n_segs;
-  uint32_t total_units;  // sum over segments of heads * q_tiles * key_tiles
   int total_tiles;       // sum over segments of heads * q_tiles
   int dp_tiles;          // tiles run whole, one work-group each (full rounds)
-  uint32_t sk_unit_begin;  // first unit of the split tiles (= unit of tile dp_tiles)
-  int n_workers;         // work-groups sharing the split tiles' units (0: none)
+  int split_tiles;       // the remaining tiles (total_tiles - dp_tiles), each cut into
+  int n_split;           // n_split equal key ranges (pieces), one work-group per piece
   const uint16_t* k_ring;
   const uint16_t* v_ring;
   int64_t slot_elems;
   int W, N, gw, H;
   float c_log2;          // scale * log2(e)
-  float* partial;        // workspace: 2 * n_workers partial results of kPartFloats
+  float* partial;        // workspace: split_tiles * n_split partial results of kPartFloats
   // Window mode (non-NULL): the ring's buffers and window come from this device
   // descriptor when the kernels run, and every segment attends over the whole
-  // window; per-segment context fields and unit counts are then derived on the
-  // device (key tiles per query tile = window keys / kAttnBlockN, the same for all).
+  // window (per-segment context fields are then derived on the device).
   const DevRing* ring_dev;
   RopeTables tab;
   FrameShift fs;

@@ -600,21 +600,6 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   }
 }
 
-// The contiguous unit range [r0, r1) of worker v out of P over U units.
-__device__ __forceinline__ uint32_t range_start(uint32_t v, uint32_t U, uint32_t P) {
-  return (uint32_t)(((uint64_t)v * U) / P);
-}
-
-// How a launch's work units (query tile x key tile) are numbered.  With host
-// context ranges the counts come with the arguments; in window mode every
-// segment has the window's key tiles, so a segment's first unit is its first
-// tile times that count.
-struct Units {
-  uint32_t total;     // all units of the launch
-  uint32_t sk_begin;  // first unit of the split tiles
-  uint32_t kt;        // window mode: key tiles per query tile (0: per segment)
-};
-
 // The launch's context in window mode: the ring descriptor as the device holds it
 // now (capacity clamped to the validated one, at least one frame of the window).
 __device__ __forceinline__ CtxView window_view(const AttnArgs& a) {
@@ -626,31 +611,35 @@ __device__ __forceinline__ CtxView window_view(const AttnArgs& a) {
   return CtxView{r->k, r->v, W, (int)mod_pos(r->first, W), keys, (keys + kBlockN - 1) / kBlockN};
 }
 
-__device__ __forceinline__ Units launch_units(const AttnArgs& a, const CtxView& wv) {
-  if (!a.ring_dev) return Units{a.total_units, a.sk_unit_begin, 0u};
-  const uint32_t kt = (uint32_t)wv.key_tiles;
-  return Units{(uint32_t)a.total_tiles * kt, (uint32_t)a.dp_tiles * kt, kt};
-}
-
-__device__ __forceinline__ uint32_t seg_unit_begin(const AttnArgs& a, const Units& un, int s) {
-  return un.kt ? (uint32_t)a.seg[s].tile_begin * un.kt : a.seg[s].unit_begin;
-}
-
-// Segment of unit u.
-__device__ __forceinline__ int unit_segment(const AttnArgs& a, const Units& un, uint32_t u) {
-  int si = 0;
-#pragma unroll
-  for (int s = 1; s < kMaxSegments; ++s)
-    if (s < a.n_segs && u >= seg_unit_begin(a, un, s)) si = s;
-  return si;
-}
-
 // The context of segment sg: the window (window mode) or its own range.
 __device__ __forceinline__ CtxView seg_view(const AttnArgs& a, const SegDev& sg, const CtxView& wv) {
   if (a.ring_dev) return wv;
   const int W = a.W;
   return CtxView{a.k_ring, a.v_ring, W, (sg.ctx_slot0 + (int)(frame_shift(a.fs) % W)) % W, sg.ctx_keys,
                  sg.key_tiles};
+}
+
+// Segment of query tile `tile` (segments are found by their first tile).
+__device__ __forceinline__ int tile_segment(const AttnArgs& a, int tile) {
+  int si = 0;
+#pragma unroll
+  for (int s = 1; s < kMaxSegments; ++s)
+    if (s < a.n_segs && tile >= a.seg[s].tile_begin) si = s;
+  return si;
+}
+
+// Key tiles [ka, kb) of piece c of a query tile cut into n_split equal key ranges.
+__device__ __forceinline__ int piece_begin(int c, int key_tiles, int n_split) { return c * key_tiles / n_split; }
+
+// Work-group -> (split tile, piece) of the last round(s): pieces are numbered
+// piece-major (all tiles' piece 0, then piece 1, ...) and dealt XCD-contiguously,
+// so the work-groups of one XCD run the same key range of consecutive query tiles
+// of one head at the same time and share those keys and values in their L2.
+__device__ __forceinline__ void split_piece(const AttnArgs& a, int b, int* tile, int* c) {
+  const int n_pieces = a.split_tiles * a.n_split;
+  const int pi = xcd_tile(b, n_pieces);
+  *c = pi / a.split_tiles;
+  *tile = a.dp_tiles + (pi - *c * a.split_tiles);
 }
 
 // kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
@@ -661,49 +650,31 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   CtxView wv{};
   if (a.ring_dev) wv = window_view(a);
+  int tile, c = 0;
   if ((int)blockIdx.x < a.dp_tiles) {
-    // whole query tiles, one per work-group, in XCD-contiguous order
-    const int tile = xcd_tile(blockIdx.x, a.dp_tiles);
-    const uint32_t u = (uint32_t)tile;  // tile index; segments are found by their first tile
-    int si = 0;
-#pragma unroll
-    for (int s = 1; s < kMaxSegments; ++s)
-      if (s < a.n_segs && u >= (uint32_t)a.seg[s].tile_begin) si = s;
-    const SegDev& sg = a.seg[si];
-    const CtxView cv = seg_view(a, sg, wv);
-    const int tl = tile - sg.tile_begin;
-    const int h = tl / sg.q_tiles;
-    run_item<kSmallN>(a, lds, sg, cv, h, tl - h * sg.q_tiles, 0, cv.key_tiles, nullptr);
+    tile = xcd_tile(blockIdx.x, a.dp_tiles);  // whole query tiles in XCD-contiguous order
+  } else {
+    split_piece(a, (int)blockIdx.x - a.dp_tiles, &tile, &c);
+  }
+  const SegDev& sg = a.seg[tile_segment(a, tile)];
+  const CtxView cv = seg_view(a, sg, wv);
+  const int tl = tile - sg.tile_begin;
+  const int h = tl / sg.q_tiles;
+  const int qt = tl - h * sg.q_tiles;
+  if ((int)blockIdx.x < a.dp_tiles) {
+    run_item<kSmallN>(a, lds, sg, cv, h, qt, 0, cv.key_tiles, nullptr);
     return;
   }
-  // the remaining tiles: equal contiguous ranges of key-tile units per worker
-  const Units un = launch_units(a, wv);
-  const uint32_t P = (uint32_t)a.n_workers;
-  const uint32_t v = (uint32_t)xcd_tile(blockIdx.x - a.dp_tiles, a.n_workers);
-  const uint32_t span = un.total - un.sk_begin;
-  const uint32_t r0 = un.sk_begin + range_start(v, span, P);
-  const uint32_t r1 = un.sk_begin + range_start(v + 1, span, P);
-  for (uint32_t u = r0; u < r1;) {
-    const int si = unit_segment(a, un, u);
-    const SegDev& sg = a.seg[si];
-    const CtxView cv = seg_view(a, sg, wv);
-    const uint32_t local = u - seg_unit_begin(a, un, si);
-    const int tl = (int)(local / (uint32_t)cv.key_tiles);
-    const int ka = (int)local - tl * cv.key_tiles;
-    const int kb = (int)min((uint32_t)cv.key_tiles, (uint32_t)ka + (r1 - u));
-    const int h = tl / sg.q_tiles;
-    const int qt = tl - h * sg.q_tiles;
-    float* part = a.partial + (size_t)(2 * v + (u == r0 ? 0 : 1)) * kPartFloats;
-    __syncthreads();  // the previous item's LDS reads are done
-    run_item<kSmallN>(a, lds, sg, cv, h, qt, ka, kb, part);
-    u += (uint32_t)(kb - ka);
-  }
+  // one of the n_split key ranges of a split tile: a partial result for the merge
+  const int ka = piece_begin(c, cv.key_tiles, a.n_split);
+  const int kb = piece_begin(c + 1, cv.key_tiles, a.n_split);
+  if (ka == kb) return;  // window mode: fewer key tiles at run time than pieces (the merge skips it)
+  float* part = a.partial + (size_t)((tile - a.dp_tiles) * a.n_split + c) * kPartFloats;
+  run_item<kSmallN>(a, lds, sg, cv, h, qt, ka, kb, part);
 }
 
-// Merge the pieces of the query tile whose key tiles start in worker v's
-// range and continue past it: worker v holds the first piece (in its slot 0
-// if the tile starts its range, else slot 1), the following workers the
-// next pieces (their slot 0).  O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i.
+// Merge the n_split pieces of split tile dp_tiles + blockIdx.x:
+// O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i, M = max m_i (pieces in order).
 // Thread t merges row t/2, dims 8c + 4(t%2) + 0..3 of every chunk c: the loads
 // of a wave read 1 KB contiguous.  The bf16 rows are staged in LDS (16-byte
 // chunk c of row r at position c ^ (r mod 16)) and written 256 bytes per row.
@@ -712,59 +683,45 @@ __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t img[kPartRows * kHeadDim];
   CtxView wv{};
   if (a.ring_dev) wv = window_view(a);
-  const Units un = launch_units(a, wv);
-  const uint32_t P = (uint32_t)a.n_workers;
-  const uint32_t span = un.total - un.sk_begin;
-  const uint32_t v = blockIdx.x;
-  const uint32_t r0 = un.sk_begin + range_start(v, span, P);
-  const uint32_t r1 = un.sk_begin + range_start(v + 1, span, P);
-  if (r1 <= r0) return;  // an empty range (not produced by the host's worker count)
-  const uint32_t last = r1 - 1;
-  const int si = unit_segment(a, un, last);
-  const SegDev& sg = a.seg[si];
-  const uint32_t kt = (uint32_t)seg_view(a, sg, wv).key_tiles;
-  const uint32_t ub = seg_unit_begin(a, un, si);
-  const uint32_t tl = (last - ub) / kt;
-  const uint32_t t0 = ub + tl * kt;  // the tile's units [t0, t1)
-  const uint32_t t1 = t0 + kt;
-  if (t0 < r0 || t1 <= r1) return;  // started in an earlier range, or not split
-  const int h = (int)tl / sg.q_tiles;
-  const int qt = (int)tl - h * sg.q_tiles;
+  const int tile = a.dp_tiles + (int)blockIdx.x;
+  const SegDev& sg = a.seg[tile_segment(a, tile)];
+  const int kt = seg_view(a, sg, wv).key_tiles;
+  const int tl = tile - sg.tile_begin;
+  const int h = tl / sg.q_tiles;
+  const int qt = tl - h * sg.q_tiles;
   const int r = threadIdx.x >> 1;  // row inside the query tile
   const int jh = threadIdx.x & 1;  // which four of each chunk's eight dims
+  const float* base = a.partial + (size_t)blockIdx.x * a.n_split * kPartFloats;
 
-  // Workers with an empty range wrote no piece (window mode: the worker count was
-  // fixed for the window at the call, the window at run time may be smaller).
   float M = -INFINITY;
-  for (uint32_t w = v; w < P && un.sk_begin + range_start(w, span, P) < t1; ++w) {
-    if (range_start(w + 1, span, P) == range_start(w, span, P)) continue;
-    const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
-    M = fmaxf(M, p[kPartRows * kHeadDim + r]);
+  for (int c = 0; c < a.n_split; ++c) {
+    if (piece_begin(c, kt, a.n_split) == piece_begin(c + 1, kt, a.n_split)) continue;  // no piece
+    M = fmaxf(M, base[(size_t)c * kPartFloats + kPartRows * kHeadDim + r]);
   }
   f32x4 acc[kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q = 0; q < kChunks; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
-  for (uint32_t w = v; w < P && un.sk_begin + range_start(w, span, P) < t1; ++w) {
-    if (range_start(w + 1, span, P) == range_start(w, span, P)) continue;
-    const float* p = a.partial + (size_t)(2 * w + (w == v && t0 != r0 ? 1 : 0)) * kPartFloats;
+  for (int c = 0; c < a.n_split; ++c) {
+    if (piece_begin(c, kt, a.n_split) == piece_begin(c + 1, kt, a.n_split)) continue;
+    const float* p = base + (size_t)c * kPartFloats;
     const float sc = __builtin_amdgcn_exp2f(p[kPartRows * kHeadDim + r] - M);
     L += sc * p[kPartRows * kHeadDim + kPartRows + r];
     const float* src = p + r * 8 + 4 * jh;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const f32x4 x = *(const f32x4*)(src + c * kPartRows * 8);
-      acc[c][0] += sc * x[0];
-      acc[c][1] += sc * x[1];
-      acc[c][2] += sc * x[2];
-      acc[c][3] += sc * x[3];
+    for (int q = 0; q < kChunks; ++q) {
+      const f32x4 x = *(const f32x4*)(src + q * kPartRows * 8);
+      acc[q][0] += sc * x[0];
+      acc[q][1] += sc * x[1];
+      acc[q][2] += sc * x[2];
+      acc[q][3] += sc * x[3];
     }
   }
   const float inv = 1.0f / L;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const u32x2 w = {pack2(acc[c][0] * inv, acc[c][1] * inv), pack2(acc[c][2] * inv, acc[c][3] * inv)};
-    *(u32x2*)(img + r * kHeadDim + (c ^ (r & 15)) * 8 + 4 * jh) = w;
+  for (int q = 0; q < kChunks; ++q) {
+    const u32x2 w = {pack2(acc[q][0] * inv, acc[q][1] * inv), pack2(acc[q][2] * inv, acc[q][3] * inv)};
+    *(u32x2*)(img + r * kHeadDim + (q ^ (r & 15)) * 8 + 4 * jh) = w;
   }
   __syncthreads();
   const int q = threadIdx.x & (kChunks - 1);  // 16-byte chunk of the row
@@ -785,14 +742,14 @@ hipError_t prepare_window_attn() {
 }
 
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.dp_tiles + a.n_workers));
+  const dim3 grid((unsigned)(a.dp_tiles + a.split_tiles * a.n_split));
   if (a.N < kBlockN)
     hipLaunchKernelGGL(window_attn_kernel<true>, grid, dim3(kThreads), kLdsBytes, s, a);
   else
     hipLaunchKernelGGL(window_attn_kernel<false>, grid, dim3(kThreads), kLdsBytes, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_workers == 0) return e;
-  hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.n_workers), dim3(2 * kPartRows), 0, s, a);
+  if (e != hipSuccess || a.split_tiles == 0 || a.n_split == 1) return e;
+  hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.split_tiles), dim3(2 * kPartRows), 0, s, a);
   return hipGetLastError();
 }
 
