@@ -260,7 +260,7 @@ def main():
     # ---- extras (not part of the timed steps): denoise-only launch, the cache-update
     # pass alone, standalone RoPE, cold/warm single calls, the 30-step dynamic fill ----
     denoise_ms = rope_ms = update_ms = None
-    dynamic = projection = replay = share = None
+    dynamic = projection = replay = share = rawk = grouped = tiny = None
     cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
@@ -290,7 +290,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         update_ms = e0.elapsed_time(e1) / reps
-        dynamic = dynamic_fill(rf, ctx, W, N, H, D, pool, stream)
+        rawk = keys_rotated_on_load(rf, ctx, cache, written, last_s, p, g, stream)
+        dynamic = dynamic_fill(rf, ctx, W, N, H, D, pool, pool_bits, stream)
+        grouped = grouped_roll(rf, ctx, g, stream)
+        tiny = tiny_window(rf, synth, stream)
         projection = qkv_projection(rf, synth, g, ctx, W, stream)
         share = hybrid_share(rf, synth, W, stream)
         replay = graph_replay(rf, synth, g, W, pool)
@@ -415,37 +418,62 @@ def main():
         out["hybrid_share_3_heads"] = share
     if replay is not None:
         out["graph_replay_30_steps"] = replay
+    if rawk is not None:
+        out["keys_rotated_on_load"] = rawk
+    if grouped is not None:
+        out["grouped_roll_30_layers"] = grouped
 
     if not args.no_cpu_baseline:
         ctx_frames = [written[t] for t in range(last_s - 6, last_s + 15)]
         _, _, qa_bits, qb_bits = pool_bits[(last_s - s0) % args.pool]
         out["cpu_baseline"] = cpu_baseline(args, g, last_s, ctx_frames, qa_bits, oa, qb_bits, ob)
+        if tiny is not None:
+            out["cpu_baseline"]["tiny_window"] = oracle_tiny(g_tiny=synth.TINY, tiny=tiny)
+        if dynamic is not None:
+            out["cpu_baseline"]["dynamic_steps"] = oracle_dynamic_steps(g, dynamic.pop("_keep"))
+    if dynamic is not None:
+        dynamic.pop("_keep", None)
 
     print(json.dumps(out), flush=True)
 
 
-def dynamic_fill(rf, ctx, W, N, H, D, pool, stream):
+DYNAMIC_ORACLE_STEPS = (0, 6, 7, 29)
+
+
+def dynamic_fill(rf, ctx, W, N, H, D, pool, pool_bits, stream):
     """The 30-step dynamic fill from an empty ring: step s rolls frames max(s-1, 0) ..
     s+14 (the clean re-encode of frame s-1 rewrites its slot) and runs the denoise
     segment (query frames s..s+14) over the min(s, 6) + 15 frames s-min(s,6) .. s+14:
     15, 16, .. 21 context frames, then 21 with one eviction per step.  Inputs cycle
     through the step pool (synthetic; parity of this loop is a GPU test).  Timed as one
-    stretch of 30 steps after one untimed pass."""
+    stretch of 30 steps after one untimed pass, which also keeps the outputs and context
+    frames of steps 0, 6, 7 and 29 for the oracle's timing."""
     import torch
 
     o = torch.empty((15 * N, H, D), dtype=torch.bfloat16, device=pool[0]["qa"].device)
+    keep = {}
 
-    def run(cache):
+    def run(cache, record=False):
+        written = {}
         for s in range(30):
-            p = pool[s % len(pool)]
+            i = s % len(pool)
+            p = pool[i]
+            ks, vs, qa_bits, _ = pool_bits[i]
+            first = 0 if s == 0 else s - 1
+            j0 = 1 if s == 0 else 0
             if s == 0:
                 cache.roll(p["k"][N:], p["v"][N:], 0)
             else:
                 cache.roll(p["k"], p["v"], s - 1)
+            for j in range(j0, 16):
+                written[first + j - j0] = (ks[j], vs[j])
             c = min(s, 6)
             rf.window_attention(ctx, cache, [rf.Segment(p["qa"], s, o, s - c, c + 15)])
+            if record and s in DYNAMIC_ORACLE_STEPS:
+                keep[s] = dict(out=o.view(torch.int16).cpu().numpy().view(np.uint16), q=qa_bits,
+                               ctx=[written[t] for t in range(s - c, s + 15)], ctx_t0=s - c)
 
-    run(rf.KVCache(ctx, W))
+    run(rf.KVCache(ctx, W), record=True)
     cache = rf.KVCache(ctx, W)  # an empty ring again, allocated before the timed stretch
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -457,7 +485,180 @@ def dynamic_fill(rf, ctx, W, N, H, D, pool, stream):
     flops = sum(4.0 * 15 * N * (min(s, 6) + 15) * N * H * D for s in range(30))
     res = {"steps": 30, "context_frames": [min(s, 6) + 15 for s in range(30)],
            "ms_total": round(ms, 3), "ms_per_step": round(ms / 30, 4),
-           "TFLOP": round(flops / 1e12, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2)}
+           "TFLOP": round(flops / 1e12, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+           "_keep": keep}
+    return res
+
+
+def keys_rotated_on_load(rf, ctx, cache, written, s, p, g, stream, reps=10):
+    """Ablation of rotating keys once when they enter the ring: rf_window_attention_rawk
+    keeps the same window's keys un-rotated and rotates every key tile as it is staged
+    (once per query tile that reads it), on the batched step's two segments; next to
+    the shipped launch on the rotated ring, same queries, same window."""
+    import torch
+
+    N, H, D, W = g.tokens_per_frame, g.n_heads, g.head_dim, g.window
+    dev = torch.device("cuda:0")
+    raw = rf.KVCache(ctx, W)
+    raw.desc.first, raw.desc.count = cache.first, cache.count
+    raw.v.copy_(cache.v)
+    for t in range(s - 6, s + 15):  # raw keys head-major (torch permute: setup, untimed)
+        kb = torch.from_numpy(np.ascontiguousarray(written[t][0]).view(np.int16)).to(dev)
+        raw.k[t % W] = kb.view(torch.bfloat16).view(N, H, D).permute(1, 0, 2)
+    oa = torch.empty_like(p["qa"])
+    ob = torch.empty_like(p["qb"])
+    res = {}
+    for name, fn, c in (("rotated_once_in_ring_ms", rf.window_attention, cache),
+                        ("rotated_per_tile_on_load_ms", rf.window_attention_rawk, raw)):
+        segs = [rf.Segment(p["qa"], s, oa, s - 6, 21), rf.Segment(p["qb"], s - 1, ob, s - 6, 21)]
+        fn(ctx, c, segs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(ctx, c, segs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+    res["slowdown"] = round(res["rotated_per_tile_on_load_ms"] / res["rotated_once_in_ring_ms"], 4)
+    del raw
+    return res
+
+
+def grouped_roll(rf, ctx, g, stream, layers=30, reps=10):
+    """The 1-frame roll (cache update: one clean frame into each layer's ring, evicting
+    the oldest) for `layers` layers: ONE rf_kvcache_roll_layers launch against `layers`
+    separate rf_kvcache_roll launches, cold (a 1 GiB fill evicts L2 and the MALL before
+    each rep) and warm.  Algorithmic bytes: 2 B read + 2 B written per K and V element.
+    Synthetic inputs; the rings start full (frames 0..20) and every rep rolls frame 21
+    again (an overwrite in place after the first)."""
+    import torch
+
+    N, H, D, W = g.tokens_per_frame, g.n_heads, g.head_dim, g.window
+    dev = torch.device("cuda:0")
+    caches = [rf.KVCache(ctx, W) for _ in range(layers)]
+    for c in caches:
+        c.desc.first, c.desc.count = 0, W
+    rings = rf.DeviceRings(caches)
+    torch.manual_seed(3)
+    k = torch.randn((layers, N, H, D), device=dev).to(torch.bfloat16)
+    v = torch.randn((layers, N, H, D), device=dev).to(torch.bfloat16)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    nbytes = layers * N * H * D * 2 * 4
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def separate():
+        for l, c in enumerate(caches):
+            c.roll(k[l], v[l], 21)
+
+    def busy():
+        try:
+            torch.cuda._sleep(100000)
+        except Exception:
+            pass
+
+    res = {"layers": layers, "frames": 1, "bytes": nbytes}
+    for name, fn in (("grouped", lambda: rings.roll(k, v, 21)), ("separate", separate)):
+        fn()
+        cold, warm = [], []
+        for _ in range(reps):
+            flush.zero_()
+            e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+            busy()
+            e0.record(stream); fn(); e1.record(stream); torch.cuda.synchronize()
+            warm.append(e0.elapsed_time(e1))
+        c_ms, w_ms = float(np.median(cold)), float(np.median(warm))
+        res[name] = {"cold_ms": round(c_ms, 4), "warm_ms": round(w_ms, 4),
+                     "cold_hbm_frac": round(nbytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "warm_hbm_frac": round(nbytes / (w_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del flush, caches, rings
+    return res
+
+
+def tiny_window(rf, synth, stream):
+    """The tiny configuration: 6x8 grid (48 tokens per frame), 12 heads of 128, a 5-slot
+    ring; frames 0-1 rolled in first, then frames 2-4 rolled and attended by query frames
+    2-4 (144 queries) over frames 0-4 (240 keys).  Returns the GPU output and inputs for
+    the oracle's timing and parity."""
+    import torch
+
+    g = synth.TINY
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cfg = synth.WORKLOAD_IDS["tiny"]
+    k = synth.frames(g, cfg, 0, 0, 5, synth.K)
+    v = synth.frames(g, cfg, 0, 0, 5, synth.V)
+    q = synth.frames(g, cfg, 0, 2, 3, synth.Q)
+    ctx = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, 64)
+    cache = rf.KVCache(ctx, g.window)
+    cache.roll(up(k[:2 * N]), up(v[:2 * N]), 0)
+    o = torch.empty((3 * N, H, D), dtype=torch.bfloat16, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    cache.roll(up(k[2 * N:]), up(v[2 * N:]), 2)
+    rf.window_attention(ctx, cache, [rf.Segment(up(q), 2, o, 0, 5)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return dict(k=k, v=v, q=q, out=o.view(torch.int16).cpu().numpy().view(np.uint16),
+                gpu_ms=e0.elapsed_time(e1))
+
+
+def _parity(got_bits, want):
+    from oracle import bf16 as obf
+    got = obf.bits_to_f64(got_bits)
+    d = np.abs(got - want)
+    return {"max_abs": float(d.max()), "mean_abs": float(d.mean()),
+            "rel_l2": float(np.linalg.norm((got - want).ravel()) / np.linalg.norm(want.ravel()))}
+
+
+def oracle_tiny(g_tiny, tiny):
+    """The oracle on the whole tiny configuration (144 queries x 240 keys x 12 heads)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+    from oracle import bf16 as obf
+    g = g_tiny
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1, user_api="blas"):
+        want = oatt.window_attention(obf.bits_to_f64(tiny["q"]), 2, obf.bits_to_f64(tiny["k"]),
+                                     obf.bits_to_f64(tiny["v"]), 0, g.grid_h, g.grid_w, g.pairs, g.base,
+                                     workers=1)
+    secs = time.perf_counter() - t0
+    flops = 4.0 * 3 * N * 5 * N * H * D
+    return {"queries": 3 * N, "keys": 5 * N, "seconds": round(secs, 4), "cores": 1,
+            "TFLOP/s": round(flops / secs / 1e12, 6), "gpu_ms_roll_and_attention": round(tiny["gpu_ms"], 4),
+            "parity": _parity(tiny["out"], want)}
+
+
+def oracle_dynamic_steps(g, keep):
+    """The oracle on whole steps of the 30-step fill (all 23,400 queries x 12 heads over
+    15, 21, 21 and 21 context frames at steps 0, 6, 7, 29), with parity against the GPU
+    output of the same step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+    from oracle import bf16 as obf
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    workers = max(1, len(os.sched_getaffinity(0)))
+    res = {}
+    for s, kp in sorted(keep.items()):
+        k = obf.bits_to_f64(np.concatenate([f[0] for f in kp["ctx"]]))
+        v = obf.bits_to_f64(np.concatenate([f[1] for f in kp["ctx"]]))
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1, user_api="blas"):
+            want = oatt.window_attention(obf.bits_to_f64(kp["q"]), s, k, v, kp["ctx_t0"], g.grid_h, g.grid_w,
+                                         g.pairs, g.base, block=64, workers=workers)
+        secs = time.perf_counter() - t0
+        flops = 4.0 * 15 * N * len(kp["ctx"]) * N * H * D
+        res[str(s)] = {"context_frames": len(kp["ctx"]), "seconds": round(secs, 2), "cores": workers,
+                       "TFLOP/s": round(flops / secs / 1e12, 6), "parity": _parity(kp["out"], want)}
     return res
 
 

@@ -274,6 +274,24 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c,
                               void* stream);
 
 /*
+ * rf_window_attention_rawk -- a measurement variant of rf_window_attention for
+ * a ring whose K buffer holds UN-rotated keys ([W][H][N][D], as the caller
+ * wrote them): every K tile is rotated by 3D-RoPE as it is staged for the
+ * score products (float32 products of the bf16 key and the float32 table
+ * entries, one rounding to bf16), i.e. once for every query tile that reads
+ * it, where the library otherwise rotates each key once when it enters the
+ * ring.  It exists to measure that choice (the pages single 3D-RoPE out as a
+ * cost: "Amazon and Reactor tune Trainium for real-time video generation",
+ * section "Three problems for generic compilers").  Same arguments and
+ * results as rf_window_attention up to the keys' rounding (the float32
+ * rotation may differ from the ring's float64 one by one bf16 step); frames
+ * of fewer than 64 tokens give RF_ERR_SHAPE.
+ */
+rf_status rf_window_attention_rawk(const rf_ctx* ctx, const rf_kvcache* c,
+                                   const rf_attn_segment* segs, int32_t n_segs, float scale,
+                                   void* stream);
+
+/*
  * rf_window_attention_noalloc -- rf_window_attention for callers that cannot
  * allocate or free device memory once set up (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation): the same validation,

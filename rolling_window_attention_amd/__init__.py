@@ -32,7 +32,7 @@ EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_r
            "rf_kvcache_bytes", "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention",
            "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift",
            "rf_window_attention_noalloc", "rf_kvcache_upload", "rf_kvcache_roll_layers",
-           "rf_window_attention_dev")
+           "rf_window_attention_dev", "rf_window_attention_rawk")
 
 
 class RfError(RuntimeError):
@@ -99,6 +99,8 @@ def lib():
         L.rf_window_attention.argtypes = [vp, ctypes.POINTER(KVCacheDesc),
                                           ctypes.POINTER(SegmentDesc), i32, ctypes.c_float, vp]
         L.rf_window_attention.restype = i32
+        L.rf_window_attention_rawk.argtypes = L.rf_window_attention.argtypes
+        L.rf_window_attention_rawk.restype = i32
         L.rf_window_attention_noalloc.argtypes = L.rf_window_attention.argtypes
         L.rf_window_attention_noalloc.restype = i32
         L.rf_kvcache_upload.argtypes = [vp, ctypes.POINTER(KVCacheDesc), i32, vp, vp]
@@ -330,6 +332,13 @@ def window_attention_noalloc(ctx, cache, segments, scale=0.0, stream=None):
     that overlap in time on one device race."""
     _check(lib().rf_window_attention_noalloc(ctx.handle, ctypes.byref(cache.desc), *_segments(ctx, segments),
                                              scale, _stream(stream)))
+
+
+def window_attention_rawk(ctx, cache, segments, scale=0.0, stream=None):
+    """Measurement variant (rf_window_attention_rawk): cache.k holds UN-rotated keys, and
+    the kernel rotates every key tile as it stages it."""
+    _check(lib().rf_window_attention_rawk(ctx.handle, ctypes.byref(cache.desc), *_segments(ctx, segments),
+                                          scale, _stream(stream)))
 
 
 def _segments(ctx, segments):

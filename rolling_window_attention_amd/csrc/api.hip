@@ -531,6 +531,7 @@ rf_status build_attn_args(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_
     d.q_tiles = (d.q_tokens + kAttnBlockM - 1) / kAttnBlockM;
     d.ctx_keys = (int)(s.ctx_frames * N);
     d.ctx_slot0 = (int)mod(s.ctx_t0, c->capacity);
+    d.ctx_t0 = s.ctx_t0;
     d.key_tiles = (d.ctx_keys + kAttnBlockN - 1) / kAttnBlockN;
     d.tile_begin = (int)tiles;
     tiles += (int64_t)d.q_tiles * g.n_heads;
@@ -570,6 +571,21 @@ rf_status rf_window_attention(const rf_ctx* ctx, const rf_kvcache* c, const rf_a
   AttnArgs a;
   rf_status st = build_attn_args(ctx, c, segs, n_segs, scale, a);
   if (st != RF_OK) return st;
+  a.partial = ctx->d_partial;
+  hipError_t e = launch_window_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  return RF_OK;
+}
+
+rf_status rf_window_attention_rawk(const rf_ctx* ctx, const rf_kvcache* c, const rf_attn_segment* segs,
+                                   int32_t n_segs, float scale, void* stream) {
+  g_err[0] = 0;
+  AttnArgs a;
+  rf_status st = build_attn_args(ctx, c, segs, n_segs, scale, a);
+  if (st != RF_OK) return st;
+  if (a.N < kAttnBlockN)
+    return fail(RF_ERR_SHAPE, "keys rotated on load need frames of at least %d tokens", kAttnBlockN);
+  a.rot_k = 1;
   a.partial = ctx->d_partial;
   hipError_t e = launch_window_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");

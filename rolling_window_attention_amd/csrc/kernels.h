@@ -85,6 +85,7 @@ struct SegDev {
   int q_tiles;           // ceil(q_tokens / kAttnBlockM)
   int ctx_keys;          // ctx_frames * N
   int ctx_slot0;         // ring slot of the first context frame
+  int64_t ctx_t0;        // the first context frame (for keys rotated on load)
   int key_tiles;         // ceil(ctx_keys / kAttnBlockN)
   int tile_begin;        // first query tile of this segment (over all segments)
 };
@@ -106,6 +107,7 @@ struct AttnArgs {
   // descriptor when the kernels run, and every segment attends over the whole
   // window (per-segment context fields are then derived on the device).
   const DevRing* ring_dev;
+  int rot_k;             // measurement variant: the ring holds un-rotated keys, rotated per K tile on load
   RopeTables tab;
   FrameShift fs;
 };

@@ -190,12 +190,16 @@ struct CtxView {
   int ctx_slot0;
   int ctx_keys;
   int key_tiles;
+  int64_t ctx_t0;  // absolute frame of the first context frame (keys rotated on load only)
 };
 
 // One work item: query tile qt of head h of segment sg over context cv, key
 // tiles [ka, kb).  A complete item (all key tiles) writes the normalised bf16
 // output; a piece of a split tile writes its partial result to `part`.
-template <bool kSmallN>
+// kRotK (a measurement variant): the ring holds un-rotated keys, and every K
+// tile is rotated by 3D-RoPE in float32 as it is staged into LDS, i.e. once per
+// query tile that reads it instead of once when it enters the ring.
+template <bool kSmallN, bool kRotK = false>
 __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const SegDev& sg, const CtxView& cv,
                                          int h, int qt, int ka, int kb, float* part) {
   const int tid = threadIdx.x;
@@ -253,15 +257,17 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const uint32_t k_lane = (uint32_t)k_r0 * (kHeadDim * 2u) + 16u * k_c;
   const uint32_t v_lane = (uint32_t)v_d0 * (uint32_t)N * 2u + 16u * v_kc;
   u32x4 kst[2], vst[2];
+  int kst_n = 0, kst_fr = 0, kst_lim = 0;  // kRotK: position of the tile in kst (wave-uniform)
 
   // Cursors of the next tile to load (uniform): slot and token offset of its
-  // first key, starting at key tile ka.
-  int kslot, kn;
+  // first key, starting at key tile ka; kfr counts the K cursor's frames.
+  int kslot, kn, kfr;
   {
     const int key0 = ka * kBlockN;
     const int f0 = key0 / N;
     kn = key0 - f0 * N;
     kslot = (cv.ctx_slot0 + f0) % W;
+    kfr = f0;
   }
   int kload = ka;
   int vslot = kslot, vn = kn, vload = ka;
@@ -273,8 +279,34 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     }
   };
 
+  // kRotK: rotate row i of the staged chunk in place, its key being in-frame token
+  // n of context frame fr: float32 products, one rounding to bf16.
+  const float2* tab_t = a.tab.t;
+  const float2* tab_h = a.tab.h;
+  const float2* tab_w = a.tab.w;
+  const int tab_pt = a.tab.pt, tab_ph = a.tab.ph, tab_pw = a.tab.pw;
+  const int gw = a.gw;
+  auto rotate_row = [&](int i, int fr, int n) {
+    const int row = n / gw;
+    const int col = n - row * gw;
+    const int64_t t = cv.ctx_t0 + fr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = 4 * k_c + j;
+      const float2* ptr = p < tab_pt ? tab_t + t * tab_pt + p
+                          : (p < tab_pt + tab_ph ? tab_h + row * tab_ph + (p - tab_pt)
+                                                 : tab_w + col * tab_pw + (p - tab_pt - tab_ph));
+      const float2 cs = *ptr;
+      const float x0 = bf16_to_f32(kst[i][j] & 0xFFFFu), x1 = bf16_to_f32(kst[i][j] >> 16);
+      kst[i][j] = pack2(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+    }
+  };
+
   auto load_k = [&]() {
     const int key_lim = nkeys - kload * kBlockN;  // valid keys in this tile (may be <= 0)
+    kst_n = kn;
+    kst_fr = kfr;
+    kst_lim = key_lim;
     if (!kSmallN && kn + kBlockN <= N && key_lim >= kBlockN) {
       // whole tile in one frame, all keys valid: lane offset + uniform offset
       const uint32_t base = (uint32_t)kslot * slot_b + k_head + (uint32_t)kn * (kHeadDim * 2u);
@@ -308,7 +340,12 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
         kst[i] = bload(krs, off[i]);
       }
     }
-    advance(kslot, kn);
+    kn += kBlockN;
+    while (kn >= N) {
+      kn -= N;
+      kslot = (kslot + 1 == W) ? 0 : kslot + 1;
+      ++kfr;
+    }
     ++kload;
   };
 
@@ -345,6 +382,17 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
 
   auto store_k = [&](int buf) {
     uint16_t* Kl = lds + buf * kKTile;
+    if constexpr (kRotK) {  // rows past the context's end hold zeros and stay so
+      const int b = N - kst_n;  // keys of the tile in its first frame
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = k_r0 + 32 * i;
+        if (r < kst_lim) {
+          if (r < b) rotate_row(i, kst_fr, kst_n + r);
+          else rotate_row(i, kst_fr + 1, kst_n + r - N);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) *(u32x4*)(Kl + (k_r0 + 32 * i) * kKRow + 8 * k_c) = kst[i];
   };
@@ -608,15 +656,16 @@ __device__ __forceinline__ CtxView window_view(const AttnArgs& a) {
   const int W = cap < 1 ? 1 : (cap > a.W ? a.W : cap);
   const int cnt = r->count < 1 ? 1 : (r->count > W ? W : r->count);
   const int keys = cnt * a.N;
-  return CtxView{r->k, r->v, W, (int)mod_pos(r->first, W), keys, (keys + kBlockN - 1) / kBlockN};
+  return CtxView{r->k, r->v, W, (int)mod_pos(r->first, W), keys, (keys + kBlockN - 1) / kBlockN, r->first};
 }
 
 // The context of segment sg: the window (window mode) or its own range.
 __device__ __forceinline__ CtxView seg_view(const AttnArgs& a, const SegDev& sg, const CtxView& wv) {
   if (a.ring_dev) return wv;
   const int W = a.W;
-  return CtxView{a.k_ring, a.v_ring, W, (sg.ctx_slot0 + (int)(frame_shift(a.fs) % W)) % W, sg.ctx_keys,
-                 sg.key_tiles};
+  const int64_t sh = frame_shift(a.fs);
+  return CtxView{a.k_ring, a.v_ring, W, (sg.ctx_slot0 + (int)(sh % W)) % W, sg.ctx_keys, sg.key_tiles,
+                 sg.ctx_t0 + sh};
 }
 
 // Segment of query tile `tile` (segments are found by their first tile).
@@ -645,7 +694,7 @@ __device__ __forceinline__ void split_piece(const AttnArgs& a, int b, int* tile,
 // kSmallN: frames shorter than a key tile (a tile may cover 3+ frames); the
 // general per-row frame walk is used.  Otherwise a tile straddles at most one
 // frame boundary and each row picks one of two bases.
-template <bool kSmallN>
+template <bool kSmallN, bool kRotK>
 __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   CtxView wv{};
@@ -662,7 +711,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   const int h = tl / sg.q_tiles;
   const int qt = tl - h * sg.q_tiles;
   if ((int)blockIdx.x < a.dp_tiles) {
-    run_item<kSmallN>(a, lds, sg, cv, h, qt, 0, cv.key_tiles, nullptr);
+    run_item<kSmallN, kRotK>(a, lds, sg, cv, h, qt, 0, cv.key_tiles, nullptr);
     return;
   }
   // one of the n_split key ranges of a split tile: a partial result for the merge
@@ -670,7 +719,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_attn_kernel(AttnArgs a) {
   const int kb = piece_begin(c + 1, cv.key_tiles, a.n_split);
   if (ka == kb) return;  // window mode: fewer key tiles at run time than pieces (the merge skips it)
   float* part = a.partial + (size_t)((tile - a.dp_tiles) * a.n_split + c) * kPartFloats;
-  run_item<kSmallN>(a, lds, sg, cv, h, qt, ka, kb, part);
+  run_item<kSmallN, kRotK>(a, lds, sg, cv, h, qt, ka, kb, part);
 }
 
 // Merge the n_split pieces of split tile dp_tiles + blockIdx.x:
@@ -734,19 +783,25 @@ __global__ __launch_bounds__(2 * kPartRows) void window_attn_fixup(AttnArgs a) {
 }
 
 hipError_t prepare_window_attn() {
-  hipError_t e = hipFuncSetAttribute((const void*)window_attn_kernel<false>,
+  hipError_t e = hipFuncSetAttribute((const void*)window_attn_kernel<false, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)window_attn_kernel<true>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)window_attn_kernel<true, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)window_attn_kernel<false, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  return e;
 }
 
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.dp_tiles + a.split_tiles * a.n_split));
-  if (a.N < kBlockN)
-    hipLaunchKernelGGL(window_attn_kernel<true>, grid, dim3(kThreads), kLdsBytes, s, a);
+  if (a.rot_k)  // the host admits it for frames of at least one key tile only
+    hipLaunchKernelGGL((window_attn_kernel<false, true>), grid, dim3(kThreads), kLdsBytes, s, a);
+  else if (a.N < kBlockN)
+    hipLaunchKernelGGL((window_attn_kernel<true, false>), grid, dim3(kThreads), kLdsBytes, s, a);
   else
-    hipLaunchKernelGGL(window_attn_kernel<false>, grid, dim3(kThreads), kLdsBytes, s, a);
+    hipLaunchKernelGGL((window_attn_kernel<false, false>), grid, dim3(kThreads), kLdsBytes, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_tiles == 0 || a.n_split == 1) return e;
   hipLaunchKernelGGL(window_attn_fixup, dim3((unsigned)a.split_tiles), dim3(2 * kPartRows), 0, s, a);

@@ -488,3 +488,41 @@ def test_oversized_ring_is_refused_before_any_launch():
     with pytest.raises(rf.RfError) as e:  # the binding refuses before allocating
         rf.KVCache(ctx, 449)
     assert e.value.status == 3
+
+
+def test_keys_rotated_on_load_variant_full_size():
+    """rf_window_attention_rawk (the measurement variant that keeps un-rotated keys in
+    the ring and rotates each key tile as it stages it) against the oracle on sampled
+    rows of the batched step, and within a bf16 step of the shipped kernel (its float32
+    key rotation may round differently from the ring's float64 one)."""
+    g, cfg = synth.FULL, 61
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    s = 9
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, g.window)
+    data = _fill_steady(g, cfg, s, cache)
+    assert cache.window() == list(range(s - 6, s + 15))
+    raw = rf.KVCache(ctx, g.window)  # same values, raw keys written head-major by torch
+    raw.desc.first, raw.desc.count = cache.first, cache.count
+    raw.v.copy_(cache.v)
+    for t in range(s - 6, s + 15):
+        raw.k[t % g.window] = up(data[t][0]).view(N, H, D).permute(1, 0, 2)
+    qa = synth.frames(g, cfg, s, s, 15, synth.Q)
+    qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
+    oa, ob, ra, rb = _out(g, 15), _out(g, 1), _out(g, 15), _out(g, 1)
+    rf.window_attention_rawk(ctx, raw, [rf.Segment(up(qa), s, ra, s - 6, 21), rf.Segment(up(qb), s - 1, rb, s - 6, 21)])
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), s, oa, s - 6, 21), rf.Segment(up(qb), s - 1, ob, s - 6, 21)])
+    torch.cuda.synchronize()
+    rk = RotatedKeys(g)
+    _check_rows(g, rk, data, qa, s, ra, s - 6, s + 15, sample_rows(15 * N, N, extra=64, seed=11), "rawk A")
+    _check_rows(g, rk, data, qb, s - 1, rb, s - 6, s + 15, sample_rows(N, N, extra=32, seed=12), "rawk B")
+    for got, ref in ((ra, oa), (rb, ob)):
+        d = (got.float() - ref.float()).abs()
+        assert float(d.max()) <= 2.0 ** -7, float(d.max())
+    small = _ctx(synth.TINY)
+    tc = rf.KVCache(small, synth.TINY.window)
+    k = up(synth.frames(synth.TINY, cfg, 0, 0, 2, synth.K))
+    tc.roll(k, k, 0)
+    with pytest.raises(rf.RfError) as e:  # frames shorter than a key tile
+        rf.window_attention_rawk(small, tc, [rf.Segment(k[:4], 0, k[4:8].clone(), 0, 2)])
+    assert e.value.status == 3
