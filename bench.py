@@ -304,14 +304,18 @@ def main():
         flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
         p_last = pool[(last_s - s0) % args.pool]
         # the 1-frame roll rewrites the last step's newest frame (s+14) in place
-        # a plain device copy of the 1-frame roll's bytes (9.6 MB read + 9.6 MB written):
-        # what one launch of that size costs at best
-        c_src = torch.empty(N * H * D * 2, dtype=torch.bfloat16, device=dev)
+        # plain device copies (rf_device_copy) moving the same bytes as the RoPE of Q and
+        # the 16- and 1-frame rolls: the bandwidth one launch of that size reaches at best
+        c_src = torch.empty(16 * N * H * D * 2, dtype=torch.bfloat16, device=dev)
         c_dst = torch.empty_like(c_src)
+        n_q = 15 * N * H * D
+        n_1 = N * H * D * 2
         single = {"rope3d_q": lambda: ctx.rope3d_apply(p["qa"], last_s, y=qr),
                   "roll_16": lambda: cache.roll(p_last["k"], p_last["v"], last_s - 1),
                   "roll_1": lambda: cache.roll(p_last["k"][15 * N:], p_last["v"][15 * N:], last_s + 14),
-                  "copy_roll_1_bytes": lambda: c_dst.copy_(c_src)}
+                  "copy_rope3d_q_bytes": lambda: rf.device_copy(c_dst[:n_q], c_src[:n_q]),
+                  "copy_roll_16_bytes": lambda: rf.device_copy(c_dst, c_src),
+                  "copy_roll_1_bytes": lambda: rf.device_copy(c_dst[:n_1], c_src[:n_1])}
         # Each timed call is enqueued while the GPU is still busy (behind the flush, or
         # behind torch's bounded spin kernel for the warm call), so the events measure the
         # GPU's time and not the host's launch latency on an idle GPU.
@@ -397,12 +401,18 @@ def main():
             "GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         nbytes = {"rope3d_q": rope_bytes, "roll_16": roll_bytes, "roll_1": roll_bytes // 16,
+                  "copy_rope3d_q_bytes": rope_bytes, "copy_roll_16_bytes": roll_bytes,
                   "copy_roll_1_bytes": roll_bytes // 16}
         out["cold_warm"] = {
             name: {"bytes": nbytes[name], "cold_ms": round(c, 4), "warm_ms": round(w, 4),
                    "cold_hbm_frac": round(nbytes[name] / (c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "warm_hbm_frac": round(nbytes[name] / (w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             for name, (c, w) in cold_warm.items()}
+        for name in ("rope3d_q", "roll_16", "roll_1"):  # time of the same bytes copied / kernel time
+            cc, cw = cold_warm["copy_" + name + "_bytes"]
+            kc, kw = cold_warm[name]
+            out["cold_warm"][name]["cold_frac_of_copy"] = round(cc / kc, 4)
+            out["cold_warm"][name]["warm_frac_of_copy"] = round(cw / kw, 4)
 
     if update_ms is not None:
         flops_update = 4.0 * N * lk * H * D
@@ -557,8 +567,11 @@ def grouped_roll(rf, ctx, g, stream, layers=30, reps=10):
         except Exception:
             pass
 
+    c_src = torch.empty(nbytes // 4, dtype=torch.int16, device=dev)  # bytes/2 copied = bytes moved
+    c_dst = torch.empty_like(c_src)
     res = {"layers": layers, "frames": 1, "bytes": nbytes}
-    for name, fn in (("grouped", lambda: rings.roll(k, v, 21)), ("separate", separate)):
+    for name, fn in (("grouped", lambda: rings.roll(k, v, 21)), ("separate", separate),
+                     ("copy_same_bytes", lambda: rf.device_copy(c_dst, c_src))):
         fn()
         cold, warm = [], []
         for _ in range(reps):
@@ -572,7 +585,10 @@ def grouped_roll(rf, ctx, g, stream, layers=30, reps=10):
         res[name] = {"cold_ms": round(c_ms, 4), "warm_ms": round(w_ms, 4),
                      "cold_hbm_frac": round(nbytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "warm_hbm_frac": round(nbytes / (w_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del flush, caches, rings
+    for name in ("grouped", "separate"):
+        res[name]["cold_frac_of_copy"] = round(res["copy_same_bytes"]["cold_ms"] / res[name]["cold_ms"], 4)
+        res[name]["warm_frac_of_copy"] = round(res["copy_same_bytes"]["warm_ms"] / res[name]["warm_ms"], 4)
+    del flush, caches, rings, c_src, c_dst
     return res
 
 

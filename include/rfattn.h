@@ -395,6 +395,18 @@ rf_status rf_window_attention_dev(const rf_ctx* ctx, const rf_kvcache* c,
                                   int32_t n_segs, float scale, void* stream);
 
 /*
+ * rf_device_copy -- a measurement aid, not a step of the path: copy `bytes`
+ * (a multiple of 16) from src to dst on `stream` with one plain kernel
+ * (16 bytes per thread, non-temporal loads and stores).  Its rate at a given
+ * size is the bandwidth a single launch that only moves bytes reaches, the
+ * practical ceiling for the RoPE and roll kernels, which move the same bytes
+ * and add arithmetic.  Both pointers 16-byte aligned device memory, not
+ * overlapping.  bytes == 0 is a no-op.  Errors: RF_ERR_NULL, RF_ERR_ALIGN,
+ * RF_ERR_SHAPE.  Needs no context.
+ */
+rf_status rf_device_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
  * rf_set_frame_shift / rf_add_frame_shift -- replaying a captured steady-state
  * step.  A window step repeats with every frame index one higher than the
  * step before (the window slides by one frame; "Amazon and Reactor tune

@@ -32,7 +32,7 @@ EXPORTS = ("rf_create", "rf_destroy", "rf_status_string", "rf_last_error", "rf_r
            "rf_kvcache_bytes", "rf_kvcache_roll", "rf_kvcache_plan_roll", "rf_window_attention",
            "rf_qkv_project", "rf_set_frame_shift", "rf_add_frame_shift",
            "rf_window_attention_noalloc", "rf_kvcache_upload", "rf_kvcache_roll_layers",
-           "rf_window_attention_dev", "rf_window_attention_rawk")
+           "rf_window_attention_dev", "rf_window_attention_rawk", "rf_device_copy")
 
 
 class RfError(RuntimeError):
@@ -99,6 +99,8 @@ def lib():
         L.rf_window_attention.argtypes = [vp, ctypes.POINTER(KVCacheDesc),
                                           ctypes.POINTER(SegmentDesc), i32, ctypes.c_float, vp]
         L.rf_window_attention.restype = i32
+        L.rf_device_copy.argtypes = [vp, vp, i64, vp]
+        L.rf_device_copy.restype = i32
         L.rf_window_attention_rawk.argtypes = L.rf_window_attention.argtypes
         L.rf_window_attention_rawk.restype = i32
         L.rf_window_attention_noalloc.argtypes = L.rf_window_attention.argtypes
@@ -442,3 +444,16 @@ def window_attention_dev(ctx, rings, layer, segments, scale=0.0, stream=None):
     cache = rings.caches[layer]
     _check(lib().rf_window_attention_dev(ctx.handle, ctypes.byref(cache.desc), rings.ptr(layer),
                                          *_segments(ctx, segments), scale, _stream(stream)))
+
+
+def device_copy(dst, src, stream=None):
+    """rf_device_copy of src's bytes into dst (device tensors of equal byte size): the
+    plain-copy bandwidth ceiling used to judge the bandwidth-bound kernels."""
+    for t, name in ((dst, "dst"), (src, "src")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous CUDA tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src must have the same size in bytes")
+    _check(lib().rf_device_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), nbytes,
+                                _stream(stream)))

@@ -613,6 +613,19 @@ rf_status rf_window_attention_noalloc(const rf_ctx* ctx, const rf_kvcache* c, co
   return RF_OK;
 }
 
+rf_status rf_device_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  g_err[0] = 0;
+  if (bytes == 0) return RF_OK;
+  if (!dst || !src) return fail(RF_ERR_NULL, "dst / src is NULL");
+  if (bytes < 0 || bytes % 16 != 0) return fail(RF_ERR_SHAPE, "bytes must be a non-negative multiple of 16");
+  if (!aligned16(dst) || !aligned16(src)) return fail(RF_ERR_ALIGN, "dst / src must be 16-byte aligned");
+  const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+  if (d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) return fail(RF_ERR_SHAPE, "dst and src overlap");
+  hipError_t e = launch_copy(dst, src, (uint64_t)bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "copy launch");
+  return RF_OK;
+}
+
 rf_status rf_kvcache_upload(const rf_ctx* ctx, const rf_kvcache* rings, int32_t n, rf_kvcache_dev* d_rings,
                             void* stream) {
   g_err[0] = 0;

@@ -146,5 +146,6 @@ struct UploadArgs {
   int n;
 };
 hipError_t launch_upload_rings(DevRing* dst, const UploadArgs& a, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, uint64_t bytes, hipStream_t s);
 
 }  // namespace rfattn

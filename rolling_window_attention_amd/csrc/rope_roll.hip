@@ -249,6 +249,28 @@ hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// Plain device copy, one 16-byte chunk per thread, non-temporal both ways: the
+// bandwidth one launch of a given size reaches when it only moves bytes (the
+// ceiling the RoPE and roll kernels are judged against).
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                   uint64_t n16, uint64_t base) {
+  const uint64_t i = base + (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+hipError_t launch_copy(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  const uint64_t per_launch = (uint64_t)1 << 31;  // chunks per launch: the grid stays below 2^23 blocks
+  for (uint64_t b = 0; b < n16; b += per_launch) {
+    const uint64_t n = n16 - b < per_launch ? n16 - b : per_launch;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (u32x4*)dst,
+                       (const u32x4*)src, b + n, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 __global__ void upload_rings_kernel(DevRing* dst, UploadArgs a) {
   if ((int)threadIdx.x < a.n) dst[threadIdx.x] = a.d[threadIdx.x];
 }

@@ -186,3 +186,13 @@ def test_ring_size_query_validates_its_arguments(L):
     assert L.rf_kvcache_bytes(ctypes.byref(_geom(head_dim=64, pairs=(11, 11, 10))), 21,
                               ctypes.byref(out)) == 3
     assert out.value == -1  # untouched on error
+
+
+def test_device_copy_validates_before_any_launch(L):
+    """rf_device_copy's argument errors come from the host, before anything is enqueued
+    (fake pointers are never dereferenced)."""
+    assert L.rf_device_copy(None, None, 0, None) == 0          # nothing to copy
+    assert L.rf_device_copy(None, ctypes.c_void_p(0x2000), 16, None) == 1
+    assert L.rf_device_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2001), 16, None) == 2
+    assert L.rf_device_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 17, None) == 3
+    assert L.rf_device_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1010), 32, None) == 3  # overlap

@@ -165,3 +165,13 @@ def test_roll_strided_inputs_and_errors():
         with pytest.raises(rf.RfError):
             cache.roll(kk, kk, t0)
         assert cache.window() == [10, 11]
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 19_169_280 // 2])
+def test_device_copy_bit_exact(nbytes):
+    """The bandwidth probe copies exactly (sizes below, at and above whole work-groups)."""
+    src = torch.randint(-32768, 32767, (nbytes // 2,), dtype=torch.int16, device="cuda")
+    dst = torch.zeros_like(src)
+    rf.device_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
