@@ -29,9 +29,11 @@
 // LDS image whose rows are the B-side index, and copies it out in 16-byte
 // chunks with non-temporal stores: token rows of 256 features for q and k (k
 // rotated on the way, with the roll's arithmetic), feature rows of 256 tokens
-// for v.  One persistent work-group per CU walks the tiles, numbered so that
-// each XCD walks consecutive feature tiles of one token tile (x rows reused from
-// L2), and puts the next tile's first loads in flight before its epilogue.
+// for v.  One persistent work-group per CU walks the tiles, and puts the next
+// tile's first loads in flight before its epilogue.  Tiles are numbered in groups
+// of kGroupM token tiles x all feature tiles, token tile fastest (tile_ref), and
+// dealt XCD-contiguously, so the work-groups of one XCD share a few token and
+// weight panels in its L2 at every reduction step.
 #include <type_traits>
 
 #include "device_common.h"

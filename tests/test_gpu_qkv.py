@@ -86,17 +86,22 @@ def _project(g, cache, x_bits, w_bits, t0):
     return down(q)
 
 
-@pytest.mark.parametrize("geom", [synth.TINY, synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4)])
-def test_identity_blocks_match_the_roll_bit_exact(geom):
-    """Project 3 frames, then 3 more that overwrite one and wrap the ring; ring and q
-    must equal what rolling (x, 2x) writes and -x."""
+@pytest.mark.parametrize("geom,calls", [
+    (synth.TINY, [(3, 3), (5, 3)]),
+    (synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4), [(3, 3), (5, 3)]),
+    # 16x16 grid, 10 frames per call: 10 token tiles of 256, i.e. one full group of 8
+    # token tiles in the kernel's tile order and a partial group of 2 (every tile checked)
+    (synth.Geometry(grid_h=16, grid_w=16, n_heads=3, window=12), [(0, 10), (8, 10)])])
+def test_identity_blocks_match_the_roll_bit_exact(geom, calls):
+    """Project frames, then more that overwrite some and wrap the ring (evicting); ring and
+    q must equal what rolling (x, 2x) writes and -x."""
     g = geom
     N, H, D, W = g.tokens_per_frame, g.n_heads, g.head_dim, g.window
     ctx = _ctx(g)
     cache = rf.KVCache(ctx, W)
     ref = rf.KVCache(ctx, W)
     w = _identity_weight(g)
-    for step, (t0, n) in enumerate([(3, 3), (5, 3)]):
+    for step, (t0, n) in enumerate(calls):
         print(f"identity blocks H={H}: frames {t0}..{t0 + n - 1}", flush=True)
         x = synth.layer_input(g, 11, step, t0, n)
         q = _project(g, cache, x, w, t0)
