@@ -41,9 +41,10 @@
  *
  * Notes for callers written against a plainer sketch of this interface
  * (V ring [W][H][N][D], frame counts everywhere, one ld per call):
- *   - the V ring is [W][H][D][N] (each slot transposed), so the value
- *     product reads 8 consecutive keys of one dim as one 16-byte chunk; a
- *     caller that inspects V slots transposes the last two axes;
+ *   - the V ring is [W][H][N/8][D][8]: values in blocks of 8 tokens, so the
+ *     value product reads 8 consecutive keys of one dim as one 16-byte chunk
+ *     and the roll writes whole 1 KB runs; token n, dim d of a head sits at
+ *     [n/8][d][n%8] (a caller that inspects V slots reorders the axes);
  *   - rf_rope3d_apply takes a token count (n_frames*N for whole frames) and
  *     separate input and output strides (x_ld, y_ld);
  *   - an rf_attn_segment names its queries as a token range (q_t0, q_tok0,
@@ -139,8 +140,9 @@ rf_status rf_rope3d_apply(const rf_ctx* ctx, const void* x, int64_t x_ld, void* 
  * t % capacity.  Valid frames: first .. first+count-1 (count <= capacity).
  *   k: bf16 [capacity][H][N][D] -- keys, already rotated by 3D-RoPE at their
  *      own positions, head-major inside a slot (rows of D contiguous);
- *   v: bf16 [capacity][H][D][N] -- values, transposed inside a slot so that a
- *      head's keys are contiguous for each dim.
+ *   v: bf16 [capacity][H][N/8][D][8] -- values in blocks of 8 tokens: token n,
+ *      dim d of head h at [slot][h][n/8][d][n%8] (8 consecutive keys of one
+ *      dim are one 16-byte chunk; the 128 dims of a key group are 2 KB).
  * The caller allocates both (capacity*H*N*D*2 bytes each, 16-byte aligned)
  * and zero-fills or otherwise initialises them; a new cache has count == 0.
  * The library reads and writes the descriptor only inside rf_kvcache_roll
@@ -171,8 +173,8 @@ rf_status rf_kvcache_bytes(const rf_geom* g, int32_t capacity, int64_t* bytes);
 /*
  * rf_kvcache_roll -- write n_frames new frames t0..t0+n_frames-1 into the
  * ring in one pass: keys are rotated by 3D-RoPE (bit-exact, as
- * rf_rope3d_apply) and stored head-major, values are stored transposed; no
- * separate transpose or copy pass.  Frames already in the window are
+ * rf_rope3d_apply) and stored head-major, values are stored in their 8-token
+ * blocks (transposed); no separate transpose or copy pass.  Frames already in the window are
  * overwritten in place; later frames are appended, and appending to a full
  * ring evicts the oldest frame (its slot is the one written).  Other slots
  * are left untouched.

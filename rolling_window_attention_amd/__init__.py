@@ -251,14 +251,15 @@ class Context:
 
 
 class KVCache:
-    """A ring of `capacity` frame slots: k [W, H, N, D] (rotated), v [W, H, D, N]."""
+    """A ring of `capacity` frame slots: k [W, H, N, D] (rotated), v [W, H, N/8, D, 8]
+    (values in blocks of 8 tokens: token n, dim d at [n // 8, d, n % 8])."""
 
     def __init__(self, ctx, capacity, device="cuda"):
         self.ctx = ctx
         kvcache_bytes(capacity, ctx.grid_h, ctx.grid_w, ctx.n_heads, ctx.head_dim, ctx.pairs,
                       ctx.base, ctx.max_frame)  # the size limit, before allocating
         shape_k = (capacity, ctx.n_heads, ctx.tokens_per_frame, ctx.head_dim)
-        shape_v = (capacity, ctx.n_heads, ctx.head_dim, ctx.tokens_per_frame)
+        shape_v = (capacity, ctx.n_heads, ctx.tokens_per_frame // 8, ctx.head_dim, 8)
         self.k = torch.zeros(shape_k, dtype=torch.bfloat16, device=device)
         self.v = torch.zeros(shape_v, dtype=torch.bfloat16, device=device)
         self.desc = KVCacheDesc(self.k.data_ptr(), self.v.data_ptr(), capacity, 0, 0)

@@ -36,7 +36,7 @@ __device__ __forceinline__ int64_t frame_shift(const FrameShift& s) {
 // (first, count) also by the rolls that use the descriptor.
 struct DevRing {
   uint16_t* k;       // [W][H][N][D]
-  uint16_t* v;       // [W][H][D][N]
+  uint16_t* v;       // [W][H][N/8][D][8]
   int64_t first;
   int32_t count;
   int32_t capacity;  // W
@@ -65,7 +65,7 @@ struct RollArgs {
   int64_t k_layer_stride, v_layer_stride;  // elements between layers' inputs (grid.y = layer)
   DevRing* rings;        // per-layer device descriptors (NULL: the one ring below)
   uint16_t* k_ring;      // [W][H][N][D]
-  uint16_t* v_ring;      // [W][H][D][N]
+  uint16_t* v_ring;      // [W][H][N/8][D][8]
   int64_t slot_elems;    // H*N*D
   int64_t t0;            // first new frame
   int slot0;             // t0 % W
@@ -120,7 +120,7 @@ struct ProjArgs {
   const uint16_t* w;     // [3C][w_ld]
   uint16_t* q;           // [M][q_ld]
   uint16_t* k_ring;      // [W][H][N][D]
-  uint16_t* v_ring;      // [W][H][D][N]
+  uint16_t* v_ring;      // [W][H][N/8][D][8]
   int64_t x_ld, w_ld, q_ld;
   int64_t slot_elems;    // H*N*D
   int64_t t0;            // frame of token 0

@@ -3,7 +3,8 @@
 // then k rows, then v rows; feature h*D + d of a block is dimension d of head
 // h), with an epilogue that writes the queries token-major and the keys and
 // values straight into their ring slots: keys rotated by the 3D-RoPE
-// (head-major [slot][h][n][d]), values transposed ([slot][h][d][n]).  The cache
+// (head-major [slot][h][n][d]), values transposed into 8-token blocks
+// ([slot][h][n/8][d][8]).  The cache
 // thus receives exactly what a roll of bf16 k and v would write, without k
 // and v ever reaching memory as tensors of their own.
 //
@@ -285,9 +286,11 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
       }
     }
   } else {
-    // feature rows: 32 chunks of 8 tokens each (N % 8 == 0: a chunk stays in one frame)
+    // 8-token chunks of feature rows (N % 8 == 0: a chunk stays in one frame) to the
+    // ring's [h][n/8][d][8] blocks; consecutive threads take consecutive features of
+    // one token group, so a wave writes 1 KB runs
     for (int idx = tid; idx < kTile * 32; idx += kThreads) {
-      const int fl = idx >> 5, c = idx & 31;
+      const int c = idx >> 8, fl = idx & (kTile - 1);
       if (fl >= rows_w || 8 * c >= rows_x) continue;
       const u32x4 v = *(const u32x4*)(T + fl * kORow + 8 * c);
       uint32_t n0;
@@ -296,7 +299,8 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, uint16_t* lds, cons
       if (slot >= a.W) slot -= a.W;
       const int f = fl0 + fl;
       const int h = f / kHeadDim, d = f - h * kHeadDim;
-      out_store((u32x4*)(a.v_ring + (int64_t)slot * a.slot_elems + h * head_elems + (int64_t)d * N + n0), v);
+      out_store((u32x4*)(a.v_ring + (int64_t)slot * a.slot_elems + h * head_elems + (int64_t)(n0 / 8) * 1024 + d * 8),
+                v);
     }
   }
 }

@@ -1,7 +1,8 @@
 // Bandwidth-bound kernels of librfattn (gfx950):
 //   rope3d_kernel  -- 3D-RoPE of a token-major bf16 tensor;
 //   roll_kernel    -- one-pass KV-cache roll: RoPE'd keys to head-major ring
-//                     slots, values transposed to [head][dim][token] slots.
+//                     slots, values transposed into 8-token blocks
+//                     [head][token/8][dim][8] of their slots.
 //
 // Sources: 3D-RoPE over time/height/width and the per-layer rolling KV cache
 // ("Amazon and Reactor tune Trainium for real-time video generation",
@@ -83,10 +84,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a, uint32
 // ---------------------------------------------------------------------------
 // roll: key work-groups rotate like rope3d and store head-major; value
 // work-groups give a thread an 8-token x 8-dim block of one (frame, head).
-// Values: the 8x8 bf16 block is transposed in registers and written as 8
-// rows of 16 bytes to V[slot][h][d][n] -- the transpose costs no extra pass.
-// Lane layout inside a wave: lane = 8*cc + gg, gg = token group, cc = dim
-// chunk, so every load and store instruction touches 8 runs of 128 bytes.
+// Values: the 8x8 bf16 block is transposed in registers so that each dim's 8
+// tokens form one 16-byte chunk, the chunk that V[slot][h][n/8][d][8] holds
+// for (token group n/8, dim d) -- the transpose costs no extra pass.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   // in[j] = 8 dims of token j (word w holds dims 2w, 2w+1);
@@ -113,10 +113,11 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // tokens).  Each thread loads 8 tokens x 8 dims (every load instruction of a
 // wave reads whole 128-byte lines, one per token), transposes them in
 // registers and writes the result into an LDS image [dim][token] of the block;
-// then every dim row of the block leaves as one run of 2 * kVBlock bytes.
-// Measured against the register transpose stored directly (8 runs of 128 bytes
-// per store instruction, none line-aligned since a row is 2N = 3120 bytes for
-// N = 1560): 65 instead of 69 us for the 16-frame roll.  Work-groups owning
+// then each 8-token group leaves as its 64 dims' chunks, one contiguous 1 KB
+// run (the value layout [h][n/8][d][8] makes a token group's dims adjacent).
+// With the earlier [h][d][n] layout each dim row of the block was a 256-byte
+// run at a 3,120-byte stride, none line-aligned, and the 16-frame roll took
+// 62-64 us cold against 55.6 us with whole 1 KB runs.  Work-groups owning
 // fewer dims per token read partial lines that a work-group on another XCD
 // fetches again, which measured much slower.
 constexpr int kVBlock = 128;  // tokens per value work-group (multiple of 8)
@@ -208,10 +209,11 @@ __global__ __launch_bounds__(256) void roll_kernel(RollArgs a, uint32_t v_blocks
     for (int i = 0; i < 8; ++i) *(u32x4*)&tile[c * 8 + i][g * 8] = vt[i];
   }
   __syncthreads();
-  uint16_t* vout = a.v_ring + (int64_t)slot * a.slot_elems + ((int64_t)h * 128 + dh * 64) * N + t0;
-  for (uint32_t q = threadIdx.x; q < 64 * ng; q += 256) {  // (dim row, group)
-    const uint32_t r = q / ng, g = q - r * ng;
-    *(u32x4*)(vout + (int64_t)r * N + g * 8) = *(const u32x4*)&tile[r][g * 8];
+  // token group t0/8 + g, dims dh*64 + r: [h][n/8][d][8]
+  uint16_t* vout = a.v_ring + (int64_t)slot * a.slot_elems + (int64_t)h * N * 128 + (int64_t)(t0 / 8) * 1024 + dh * 512;
+  for (uint32_t q = threadIdx.x; q < 64 * ng; q += 256) {  // (group, dim row): a wave writes 1 KB runs
+    const uint32_t g = q >> 6, r = q & 63u;
+    *(u32x4*)(vout + (int64_t)g * 1024 + r * 8) = *(const u32x4*)&tile[r][g * 8];
   }
 }
 

@@ -248,14 +248,15 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(cv.v_ring), 0, (int)ring_b, kBufferWord3);
   const uint32_t k_head = (uint32_t)h * (uint32_t)N * (kHeadDim * 2u);  // K: [H][N][D]
-  const uint32_t v_head = (uint32_t)h * kHeadDim * (uint32_t)N * 2u;    // V: [H][D][N]
-  // K: rows (tid>>4) + 32i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 64i, key chunk tid&7.
+  const uint32_t v_head = (uint32_t)h * kHeadDim * (uint32_t)N * 2u;    // V: [H][N/8][D][8]
+  // K: rows (tid>>4) + 32i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 64i, key chunk tid&7
+  // (8 keys of one dim: one 16-byte chunk of the ring's [n/8][d][8] blocks, 2 KB per key group).
   const int k_r0 = tid >> 4, k_c = tid & 15;
   const int v_d0 = tid >> 3, v_kc = tid & 7;
   // Lane parts of the byte offsets for a tile inside one frame; row i adds a
   // uniform 32*i rows (K) or 64*i dims (V), carried in the scalar offset.
   const uint32_t k_lane = (uint32_t)k_r0 * (kHeadDim * 2u) + 16u * k_c;
-  const uint32_t v_lane = (uint32_t)v_d0 * (uint32_t)N * 2u + 16u * v_kc;
+  const uint32_t v_lane = (uint32_t)v_d0 * 16u + 2048u * v_kc;
   u32x4 kst[2], vst[2];
   int kst_n = 0, kst_fr = 0, kst_lim = 0;  // kRotK: position of the tile in kst (wave-uniform)
 
@@ -352,27 +353,30 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   auto load_v = [&]() {
     const int key_lim = nkeys - vload * kBlockN;
     if (!kSmallN && vn + kBlockN <= N && key_lim >= kBlockN) {
-      const uint32_t base = (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u;
+      const uint32_t base = (uint32_t)vslot * slot_b + v_head + (uint32_t)(vn / 8) * 2048u;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         vst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               vrs, v_lane, base + (uint32_t)i * 128u * (uint32_t)N, 0));
+                                               vrs, v_lane, base + (uint32_t)i * 64u * 16u, 0));
     } else {
       uint32_t base;
       if constexpr (!kSmallN) {
         const int b = N - vn;
         const int nxt = (vslot + 1 == W) ? 0 : vslot + 1;
-        base = (8 * v_kc < b) ? (uint32_t)vslot * slot_b + v_head + (uint32_t)vn * 2u
-                              : (uint32_t)nxt * slot_b + v_head - (uint32_t)b * 2u;
+        // chunk c of the tile is key group vn/8 + c of this frame, or group
+        // vn/8 + c - N/8 of the next one (b and N are multiples of 8)
+        base = (8 * v_kc < b) ? (uint32_t)vslot * slot_b + v_head + (uint32_t)(vn / 8) * 2048u
+                              : (uint32_t)nxt * slot_b + v_head + (uint32_t)(vn / 8) * 2048u -
+                                    (uint32_t)(N / 8) * 2048u;
       } else {
         int n = vn + 8 * v_kc, slot = vslot;
         while (n >= N) { n -= N; slot = (slot + 1 == W) ? 0 : slot + 1; }
-        base = (uint32_t)slot * slot_b + v_head + (uint32_t)n * 2u - 16u * v_kc;
+        base = (uint32_t)slot * slot_b + v_head + (uint32_t)(n / 8) * 2048u - 2048u * v_kc;
       }
       const bool valid = 8 * v_kc < key_lim;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint32_t off = base + (uint32_t)(v_d0 + 64 * i) * (uint32_t)N * 2u + 16u * v_kc;
+        const uint32_t off = base + v_lane + (uint32_t)i * 64u * 16u;
         vst[i] = bload(vrs, valid ? off : kOutOfRange);
       }
     }

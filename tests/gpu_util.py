@@ -34,8 +34,15 @@ def ring_frame_k(cache_k_bits, slot):
 
 
 def ring_frame_v(cache_v_bits, slot):
-    """Ring V slot [H, D, N] -> token-major [N, H, D]."""
-    return cache_v_bits[slot].transpose(2, 0, 1)
+    """Ring V slot [H, N/8, D, 8] (8-token blocks) -> token-major [N, H, D]."""
+    H, G, D, _ = cache_v_bits[slot].shape
+    return cache_v_bits[slot].transpose(1, 3, 0, 2).reshape(G * 8, H, D)
+
+
+def ring_slot_v(v_bits):
+    """Token-major [N, H, D] -> a ring V slot [H, N/8, D, 8]."""
+    N, H, D = v_bits.shape
+    return v_bits.reshape(N // 8, 8, H, D).transpose(2, 0, 3, 1)
 
 
 def errors(got, want):

@@ -24,7 +24,7 @@ from rolling_window_attention_amd import synth
 from oracle import rope3d as orope
 from oracle.ring import RingModel
 
-from gpu_util import RotatedKeys, assert_close, down, f64, oracle_rows, ring_frame_k, ring_frame_v, sample_rows, up
+from gpu_util import ring_slot_v, RotatedKeys, assert_close, down, f64, oracle_rows, ring_frame_k, ring_frame_v, sample_rows, up
 
 pytestmark = pytest.mark.gpu
 
@@ -49,12 +49,12 @@ def _dev_windows(rings):
 def _expected_ring(g, model, W):
     N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
     K = np.zeros((W, H, N, D), np.uint16)
-    V = np.zeros((W, H, D, N), np.uint16)
+    V = np.zeros((W, H, N // 8, D, 8), np.uint16)
     for s in range(W):
         if model.slot_data[s] is not None:
             kb, vb, t = model.slot_data[s]
             K[s] = _spec(g, kb, t).transpose(1, 0, 2)
-            V[s] = vb.transpose(1, 2, 0)
+            V[s] = ring_slot_v(vb)
     return K, V
 
 

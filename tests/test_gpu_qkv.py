@@ -169,7 +169,7 @@ def test_full_size_sampled_tokens():
     n_of = rows % N
     slots = (t0 + f_of) % W
     got_k = Kb[slots, :, n_of, :]           # [rows, H, D]
-    got_v = Vb[slots, :, :, n_of]           # [rows, H, D]
+    got_v = Vb[slots, :, n_of // 8, :, n_of % 8]  # [rows, H, D] (8-token blocks)
     krot = _rotate_rows(g, kr, t0, rows)
     _near_rotated(got_k, krot, kr, "K sampled", ek)
     _near(got_v, vr, "V sampled", ev)
