@@ -26,21 +26,29 @@ struct RopeTables {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// float64 -> bf16, round to nearest even, taken directly (no double rounding).
-// The float32 conversion rounds to nearest even; that can only mislead the
-// second rounding when it lands exactly on a bf16 halfway point (low 16 bits
-// 0x8000) without being exact.  In that case the float32 pattern is moved one
-// float32 ulp towards the true value before the float32 -> bf16 rounding.
-// Written without branches (selects only).  Finite inputs only (NaN/Inf are
-// not produced by the library's arithmetic on finite bf16 inputs).
-__device__ __forceinline__ uint32_t f64_to_bf16(double y) {
+// Two float64 values -> a packed pair of bf16 (low = lo), each rounded to
+// nearest even directly (no double rounding).  Each value is first rounded to
+// float32 with round-to-odd -- truncated toward zero, and the last bit set when
+// that was inexact -- which keeps 16 bits more than bf16, so the second rounding
+// (v_cvt_pk_bf16_f32, to nearest even) gives the correctly rounded bf16 of the
+// float64 value (rounding to odd with at least two extra bits, then to nearest,
+// equals rounding to nearest once).  The float32 rounding of the conversion is
+// to nearest; when it went away from zero, one ulp toward zero is its
+// truncation.  Finite inputs only.
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
   const float f = (float)y;
-  uint32_t fb = __float_as_uint(f);
   const double back = (double)f;
-  const bool fix = ((fb & 0xFFFFu) == 0x8000u) && (back != y);
-  const uint32_t step = (fabs(y) > fabs(back)) ? 1u : 0xFFFFFFFFu;
-  fb += fix ? step : 0u;
-  return (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
+  uint32_t fb = __float_as_uint(f);
+  const bool inexact = back != y;
+  fb -= (inexact && fabs(back) > fabs(y)) ? 1u : 0u;
+  fb |= inexact ? 1u : 0u;
+  return __uint_as_float(fb);
+}
+typedef __bf16 rf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float rf_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f64x2_to_bf16x2(double lo, double hi) {
+  const rf_f32x2 f = {f64_to_f32_odd(lo), f64_to_f32_odd(hi)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, rf_bf16x2));
 }
 
 // (cos, sin) of rotation pair p for a token at (frame t, row r, column c).
@@ -72,7 +80,7 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, int p0, int64_t t, int r, i
     double cc = (double)cs.x, ss = (double)cs.y;
     double y0 = x0 * cc - x1 * ss;
     double y1 = x0 * ss + x1 * cc;
-    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    out[k] = f64x2_to_bf16x2(y0, y1);
   }
   u32x4 y = {out[0], out[1], out[2], out[3]};
   return y;
@@ -92,7 +100,7 @@ __device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, int p0, int64_t t, i
     double cc = (double)cs.x, ss = (double)cs.y;
     double y0 = (x0 * cc - x1 * ss) * scale;
     double y1 = (x0 * ss + x1 * cc) * scale;
-    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    out[k] = f64x2_to_bf16x2(y0, y1);
   }
   u32x4 y = {out[0], out[1], out[2], out[3]};
   return y;
@@ -126,7 +134,7 @@ __device__ __forceinline__ u32x4 rope_chunk_cs(u32x4 x, const ChunkCS& cs) {
     double x1 = (double)bf16_to_f32(in[k] >> 16);
     double y0 = x0 * cs.c[k] - x1 * cs.s[k];
     double y1 = x0 * cs.s[k] + x1 * cs.c[k];
-    out[k] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    out[k] = f64x2_to_bf16x2(y0, y1);
   }
   u32x4 y = {out[0], out[1], out[2], out[3]};
   return y;
