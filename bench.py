@@ -260,7 +260,7 @@ def main():
     # ---- extras (not part of the timed steps): denoise-only launch, the cache-update
     # pass alone, standalone RoPE, cold/warm single calls, the 30-step dynamic fill ----
     denoise_ms = rope_ms = update_ms = None
-    dynamic = projection = replay = share = rawk = grouped = tiny = None
+    dynamic = projection = replay = share = rawk = grouped = tiny = fill_replay = None
     cold_warm = {}
     rope_bytes = 15 * N * H * D * 2 * 2
     if not args.no_extras:
@@ -297,6 +297,7 @@ def main():
         projection = qkv_projection(rf, synth, g, ctx, W, stream)
         share = hybrid_share(rf, synth, W, stream)
         replay = graph_replay(rf, synth, g, W, pool)
+        fill_replay = fill_graph_replay(rf, g, W, pool)
 
         # cold (a 1 GiB fill evicts L2 and the 256 MB MALL before each rep) and warm
         # single-call times of the standalone RoPE and of the step's roll; the roll
@@ -428,6 +429,8 @@ def main():
         out["hybrid_share_3_heads"] = share
     if replay is not None:
         out["graph_replay_30_steps"] = replay
+    if fill_replay is not None:
+        out["fill_graph_replay_30_steps"] = fill_replay
     if rawk is not None:
         out["keys_rotated_on_load"] = rawk
     if grouped is not None:
@@ -836,6 +839,85 @@ def graph_replay(rf, synth, g, W, pool, steps=30):
             "gpu_ms_per_step_graph": round(gpu_graph, 4),
             "host_us_per_step_eager": round(host_eager * 1e6, 1),
             "host_us_per_step_graph": round(host_graph * 1e6, 1)}
+
+
+def fill_graph_replay(rf, g, W, pool, steps=30):
+    """The 30-step window fill from an empty ring (context 15 -> 21 frames, then one
+    eviction per step), each step = roll of the 15 current frames, denoise attention over
+    the whole window, roll of the finished clean frame.  Eagerly with host frame ranges,
+    then as 30 replays of ONE captured step that reads its window from a device ring
+    descriptor and its frame indices from the device frame shift (the ring reset on the
+    device first).  GPU time for the 30 steps (events) and host time to enqueue them."""
+    import torch
+
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    dev = torch.device("cuda:0")
+    p = pool[0]
+    kn, vn = p["k"][N:], p["v"][N:]          # 15 current frames
+    kc, vc = p["k"][:N], p["v"][:N]          # one clean frame
+    q = p["qa"]
+    o = torch.empty((15 * N, H, D), dtype=torch.bfloat16, device=dev)
+    ctx_e = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, max_frame=8192)
+    ctx_g = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, max_frame=8192)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def eager(cache):
+        for s in range(steps):
+            cache.roll(kn, vn, s)
+            c0 = max(0, s - 6)
+            rf.window_attention(ctx_e, cache, [rf.Segment(q, s, o, c0, s + 15 - c0)])
+            cache.roll(kc, vc, s)
+
+    eager(rf.KVCache(ctx_e, W))  # untimed pass
+    ce = rf.KVCache(ctx_e, W)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    h0 = time.perf_counter()
+    eager(ce)
+    host_eager = (time.perf_counter() - h0) / steps
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gpu_eager = e0.elapsed_time(e1) / steps
+
+    cg = rf.KVCache(ctx_g, W)
+    rings = rf.DeviceRings([cg])
+    shift = torch.zeros(1, dtype=torch.int64, device=dev)
+    ctx_g.set_frame_shift(shift, steps)
+    gc.collect()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            rings.roll(kn.unsqueeze(0), vn.unsqueeze(0), 0)
+            rf.window_attention_dev(ctx_g, rings, 0, [rf.Segment(q, 0, o, 0, 0)])
+            rings.roll(kc.unsqueeze(0), vc.unsqueeze(0), 0)
+            ctx_g.add_frame_shift(shift, 1)
+    stream.wait_stream(side)
+    res = {"steps": steps}
+    for rep in range(2):  # the first pass untimed
+        rings.reset()
+        shift.zero_()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        h0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        host_graph = (time.perf_counter() - h0) / steps
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gpu_graph = e0.elapsed_time(e1) / steps
+    assert int(shift.item()) == steps
+    same = bool(torch.equal(cg.k.view(torch.int16), ce.k.view(torch.int16)) and
+                torch.equal(cg.v.view(torch.int16), ce.v.view(torch.int16)))
+    ctx_g.set_frame_shift(None, 0)
+    res.update({"gpu_ms_per_step_eager": round(gpu_eager, 4), "gpu_ms_per_step_graph": round(gpu_graph, 4),
+                "host_us_per_step_eager": round(host_eager * 1e6, 1),
+                "host_us_per_step_graph": round(host_graph * 1e6, 1),
+                "rings_equal_after_30_steps": same})
+    del rings, cg, ce
+    return res
 
 
 def cpu_baseline(args, g, s, ctx_frames, qa_bits, oa, qb_bits, ob):
