@@ -56,6 +56,8 @@
 // inside a tile is permuted (kappa below) so that each lane's 16 softmax
 // values per key block are 16 consecutive keys, which is what the P^T
 // operand of the value product needs; the softmax is order-free over keys.
+// The K tile is staged into LDS already in that order (row m holds key
+// kappa(m)), so the fragment reads walk consecutive rows.
 //
 // Schedule: the eight waves form two groups (waves 0-3 and 4-7, one wave of
 // each per SIMD) that play ping-pong.  A key-tile step has two halves
@@ -252,6 +254,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   // K: rows (tid>>4) + 32i, 16-byte chunk tid&15.  V^T: dims (tid>>3) + 64i, key chunk tid&7
   // (8 keys of one dim: one 16-byte chunk of the ring's [n/8][d][8] blocks, 2 KB per key group).
   const int k_r0 = tid >> 4, k_c = tid & 15;
+  // LDS row of key k_r0 (and 32 + k_r0): the inverse of the key order kappa the
+  // score MFMAs read in (below)
+  const int k_lds = (k_r0 & 3) + 4 * ((k_r0 >> 4) & 1) + 8 * ((k_r0 >> 2) & 3);
   const int v_d0 = tid >> 3, v_kc = tid & 7;
   // Lane parts of the byte offsets for a tile inside one frame; row i adds a
   // uniform 32*i rows (K) or 64*i dims (V), carried in the scalar offset.
@@ -398,7 +403,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *(u32x4*)(Kl + (k_r0 + 32 * i) * kKRow + 8 * k_c) = kst[i];
+    for (int i = 0; i < 2; ++i) *(u32x4*)(Kl + (k_lds + 32 * i) * kKRow + 8 * k_c) = kst[i];
   };
   auto store_v = [&](int buf) {
     uint16_t* Vl = lds + 2 * kKTile + buf * kVTile;
@@ -416,9 +421,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
   f32x16 negm = {};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // A-operand row m of the score MFMA reads key kappa(m): lane half hf of
-  // output register i then holds key 16*hf + i of each 32-key block.
-  const int krow = 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
+  // A-operand row m of the score MFMA is LDS row m of the K tile, which the
+  // staging filled with key kappa(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3) (k_lds is
+  // the inverse): lane half hf of output register i then holds key 16*hf + i of
+  // each 32-key block, and a quarter-wave's fragment reads cover 16 consecutive
+  // rows, which the 272-byte row stride spreads over all LDS banks.
 
   // T^T = K Q'^T - m for keys [0,32) and [32,64) of the tile in K buffer `buf`
   // (Q' = c Q): the exponents of the softmax weights in log2 units.  All 16
@@ -435,8 +442,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     bf16x8 kf[16];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      kf[2 * s] = *(const bf16x8*)(Kl + krow * kKRow + 16 * s + 8 * hf);
-      kf[2 * s + 1] = *(const bf16x8*)(Kl + (32 + krow) * kKRow + 16 * s + 8 * hf);
+      kf[2 * s] = *(const bf16x8*)(Kl + lr * kKRow + 16 * s + 8 * hf);
+      kf[2 * s + 1] = *(const bf16x8*)(Kl + (32 + lr) * kKRow + 16 * s + 8 * hf);
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %5, %4\n\tv_mfma_f32_32x32x16_bf16 %1, %3, %5, %4"
