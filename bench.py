@@ -148,7 +148,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(librfattn has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -2,7 +2,7 @@
 
 bfloat16 is the top half of an IEEE binary32: 1 sign bit, 8 exponent bits,
 7 stored mantissa bits.  The pages never fix a precision; bf16 storage with
-float32 accumulation is the reading this build takes for the attention path.
+float32 accumulation is the reading taken here for the attention path.
 
 The conversion float64 -> bf16 here is written from the definition of
 round-to-nearest-even, not from a bit trick: scale |x| onto the integer grid

@@ -16,7 +16,7 @@ else (every other step in float64):
 
 The pages fix no precision ("A kernel-centric path to real-time video
 generation on Trainium" and its digests give none); bf16 operands with float32
-accumulation is the reading this build takes.  What the model is for: its error
+accumulation is the reading taken here.  What the model is for: its error
 against the exact oracle is what these operand roundings alone cost on given
 rows, so no bf16 implementation of this reading can be expected to do better.
 At large softmax scales that cost grows with the logits and reaches the

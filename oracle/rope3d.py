@@ -7,7 +7,7 @@ width -- where an LLM uses one position ("Amazon and Reactor tune Trainium
 for real-time video generation", section "Three problems for generic
 compilers"; "Optimizing Real-Time Video Generation on Trainium Chips",
 section 5 "Three core bottlenecks").  They give no formula; the readings
-below are the plainest ones and are listed in the design doc:
+below are the plainest ones the pages support:
 
 * Token ``i`` of a block that starts at absolute latent frame ``t0`` sits at
   ``(t, r, c) = (t0 + i // N, (i % N) // grid_w, i % grid_w)``, ``N =

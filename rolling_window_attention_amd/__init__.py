@@ -449,7 +449,7 @@ def window_attention_dev(ctx, rings, layer, segments, scale=0.0, stream=None):
 
 def device_copy(dst, src, stream=None):
     """rf_device_copy of src's bytes into dst (device tensors of equal byte size): the
-    plain-copy bandwidth ceiling used to judge the bandwidth-bound kernels."""
+    plain-copy bandwidth ceiling the bandwidth-bound kernels are measured against."""
     for t, name in ((dst, "dst"), (src, "src")):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous CUDA tensor")

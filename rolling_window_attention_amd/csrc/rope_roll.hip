@@ -253,7 +253,7 @@ hipError_t launch_roll(const RollArgs& a, hipStream_t s) {
 
 // Plain device copy, one 16-byte chunk per thread, non-temporal both ways: the
 // bandwidth one launch of a given size reaches when it only moves bytes (the
-// ceiling the RoPE and roll kernels are judged against).
+// ceiling the RoPE and roll kernels are measured against).
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                    uint64_t n16, uint64_t base) {
   const uint64_t i = base + (uint64_t)blockIdx.x * 256u + threadIdx.x;

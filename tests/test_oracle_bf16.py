@@ -1,6 +1,6 @@
 """Pins for the oracle's bf16 codec (CPU only).
 
-The pages fix no number format; bf16 storage is this build's reading.  The codec is
+The pages fix no number format; bf16 storage is the reading taken here.  The codec is
 pinned to (a) hand-derived cases of the format's definition (tests/golden/bf16_cases.txt),
 (b) a brute-force nearest-value search with exact rational arithmetic, (c) torch's
 float32 -> bfloat16 conversion on float32 inputs and (d) a round trip over all patterns.
