@@ -91,7 +91,12 @@ def _project(g, cache, x_bits, w_bits, t0):
     (synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4), [(3, 3), (5, 3)]),
     # 16x16 grid, 10 frames per call: 10 token tiles of 256, i.e. one full group of 8
     # token tiles in the kernel's tile order and a partial group of 2 (every tile checked)
-    (synth.Geometry(grid_h=16, grid_w=16, n_heads=3, window=12), [(0, 10), (8, 10)])])
+    (synth.Geometry(grid_h=16, grid_w=16, n_heads=3, window=12), [(0, 10), (8, 10)]),
+    # 5 and 6 heads (reductions of 10 and 12 steps of 64) on 384-token frames: some
+    # 256-token tiles lie inside one frame, others straddle two; 7.5 token tiles (the
+    # last half full) and, with 5 heads, a last feature tile of 128 features
+    (synth.Geometry(grid_h=16, grid_w=24, n_heads=5, window=8), [(0, 5), (4, 5)]),
+    (synth.Geometry(grid_h=16, grid_w=24, n_heads=6, window=8), [(0, 5), (4, 5)])])
 def test_identity_blocks_match_the_roll_bit_exact(geom, calls):
     """Project frames, then more that overwrite some and wrap the ring (evicting); ring and
     q must equal what rolling (x, 2x) writes and -x."""
