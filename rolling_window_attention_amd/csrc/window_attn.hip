@@ -22,7 +22,8 @@
 // (the cache-update pass alone) is split this way entirely.
 //
 // Per query tile: eight waves of 32 query rows (two per SIMD) share each K/V
-// tile, which the work-group fetches and stages once.  Per 64-key tile:
+// tile, which the work-group fetches and stages once (a wave whose rows all lie
+// past the segment's end only stages).  Per 64-key tile:
 //   T^T[key][q] = K_tile . Q'^T - m  v_mfma_f32_32x32x16_bf16, 2 key blocks x 8 k-steps
 //   online softmax in float32: 2^T, bf16 weights P, row sums
 //   O^T[d][q]  += V^T_tile . P^T     4 dim blocks x 4 k-steps
@@ -580,32 +581,49 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, uint16_t* lds, const
     load_v();  // V_1
     __syncthreads();
   }
+  // A wave whose 32 query rows all lie past the segment's end (the last query
+  // tile of a segment that is not a multiple of 256 rows) computes nothing: it
+  // only stages its share of the K/V tiles and keeps the barriers, in a loop of
+  // its own (the working waves' loop is left as it is).  Its O^T, m and l stay
+  // 0; no output row of it is ever written.
+  const bool live = __builtin_amdgcn_readfirstlane(wave) * 32 < sg.q_tokens - qt * kBlockM;
   f32x16 x0, x1;
   u32x4 pw[4];
-  for (int j = 0; j < ntiles; ++j) {
-    if (j > 0) values((j - 1) & 1, pw);
-    scores(j & 1, x0, x1);
-    __syncthreads();
-    if (j == ntiles - 1) mask_tail(kb - 1, x0, x1);
-    if (j == 0) {  // first tile: the running max starts at its row max
-      const float m0 = tile_max(x0, x1);
+  if (live) {
+    for (int j = 0; j < ntiles; ++j) {
+      if (j > 0) values((j - 1) & 1, pw);
+      scores(j & 1, x0, x1);
+      __syncthreads();
+      if (j == ntiles - 1) mask_tail(kb - 1, x0, x1);
+      if (j == 0) {  // first tile: the running max starts at its row max
+        const float m0 = tile_max(x0, x1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x0[i] -= m0;
-        x1[i] -= m0;
+        for (int i = 0; i < 16; ++i) {
+          x0[i] -= m0;
+          x1[i] -= m0;
+        }
+        m_run = m0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m0;
       }
-      m_run = m0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -m0;
+      softmax(x0, x1, pw);
+      store_k((j + 1 + grp) & 1);
+      store_v((j + grp) & 1);
+      load_k();
+      load_v();
+      __syncthreads();
     }
-    softmax(x0, x1, pw);
-    store_k((j + 1 + grp) & 1);
-    store_v((j + grp) & 1);
-    load_k();
-    load_v();
-    __syncthreads();
+    values((ntiles - 1) & 1, pw);
+  } else {
+    for (int j = 0; j < ntiles; ++j) {
+      __syncthreads();
+      store_k((j + 1 + grp) & 1);
+      store_v((j + grp) & 1);
+      load_k();
+      load_v();
+      __syncthreads();
+    }
   }
-  values((ntiles - 1) & 1, pw);
   if (grp == 0) __syncthreads();  // the same barrier count as group 1
 
   // O^T out of the accumulation registers, once the last MFMAs have drained.
