@@ -92,3 +92,49 @@ def test_random_configuration(seed):
         want = oatt.window_attention(f64(q), q_t0, f64(k), f64(v), c0, g.grid_h, g.grid_w, g.pairs, g.base,
                                      scale=scale if scale else None, q_tok0=tok0, workers=1)
         assert_close(f64(down(o)), want, f"seed {seed} segment {i}")
+
+
+# Segment lengths around the 32-row boundaries of the waves in a 256-row query tile:
+# the last tile of a segment runs only the waves that hold some of its rows, the
+# others only stage keys and values.  Checked alone (every tile of the launch cut into
+# key ranges and merged) and next to a long segment of 128 tiles per head placed last,
+# so that the short segments' tiles fall in the launch's whole-tile round.
+WAVE_EDGE_ROWS = (1, 31, 32, 33, 224, 225, 255, 256, 257, 288)
+
+
+@pytest.mark.parametrize("with_long", [False, True])
+def test_segment_lengths_at_wave_boundaries(with_long):
+    g = synth.Geometry(grid_h=8, grid_w=12, n_heads=2, window=6)
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    ctx = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, max_frame=512)
+    cache = rf.KVCache(ctx, g.window)
+    k = synth.frames(g, 77, 0, 0, g.window, synth.K)
+    v = synth.frames(g, 77, 0, 0, g.window, synth.V)
+    cache.roll(up(k), up(v), 0)
+
+    def segment(i, n_rows):
+        tok0 = (7 * i) % N
+        q = synth.frames(g, 77, 100 + i, 3, (tok0 + n_rows + N - 1) // N, synth.Q)[tok0:tok0 + n_rows]
+        o = torch.empty((n_rows, H, D), dtype=torch.bfloat16, device="cuda")
+        return rf.Segment(up(q), 3, o, 0, g.window, q_tok0=tok0), (q, tok0, o)
+
+    short = [segment(i, n) for i, n in enumerate(WAVE_EDGE_ROWS)]
+    checks = [r for _, r in short]
+    groups = [short[:7], short[7:]]
+    for gi, grp in enumerate(groups):
+        segs = [sg for sg, _ in grp]
+        if with_long:  # 256 query tiles in all: the launch's whole-tile round takes the short ones first
+            sg, ref = segment(50 + gi, 128 * 256)
+            segs.append(sg)
+            q, tok0, o = ref
+            checks.append((q[:64], tok0, o[:64]))
+            checks.append((q[-64:], (tok0 + len(q) - 64) % N, o[-64:], 3 + (tok0 + len(q) - 64) // N))
+        print(f"with_long={with_long}: segments of {[len(r[0]) for _, r in grp]} rows", flush=True)
+        rf.window_attention(ctx, cache, segs)
+    torch.cuda.synchronize()
+    for c in checks:
+        q, tok0, o = c[:3]
+        q_t0 = c[3] if len(c) > 3 else 3
+        want = oatt.window_attention(f64(q), q_t0, f64(k), f64(v), 0, g.grid_h, g.grid_w, g.pairs, g.base,
+                                     q_tok0=tok0, workers=1)
+        assert_close(f64(down(o.contiguous())), want, f"{len(q)} rows from token {tok0} (with_long={with_long})")
