@@ -51,6 +51,29 @@ def test_tiny_full_parity():
     assert_close(f64(down(o)), want, "tiny")
 
 
+def test_time_shift_by_1000_frames():
+    """The same frames placed 1,000 frames later (keys rolled at t + 1000, queries at
+    q_t0 + 1000): the output changes by rounding only, since the rotation acts on the
+    difference of positions; both launches also against the oracle at their own
+    positions."""
+    g, cfg = synth.TINY, synth.WORKLOAD_IDS["tiny"]
+    ctx = _ctx(g)
+    outs = []
+    k = synth.frames(g, cfg, 0, 0, 5, synth.K)
+    v = synth.frames(g, cfg, 0, 0, 5, synth.V)
+    q = synth.frames(g, cfg, 0, 2, 3, synth.Q)
+    for t in (0, 1000):
+        cache = rf.KVCache(ctx, g.window)
+        cache.roll(up(k), up(v), t)
+        o = _out(g, 3)
+        rf.window_attention(ctx, cache, [rf.Segment(up(q), 2 + t, o, t, 5)])
+        torch.cuda.synchronize()
+        want = oatt.window_attention(f64(q), 2 + t, f64(k), f64(v), t, g.grid_h, g.grid_w, g.pairs, g.base)
+        assert_close(f64(down(o)), want, f"frames from {t}")
+        outs.append(f64(down(o)))
+    assert_close(outs[1], outs[0], "shifted by 1000 frames against unshifted")
+
+
 def test_tiny_wrap_run_and_two_segments():
     """Twelve steps on a 5-slot ring: each step rolls the clean frame s-1 and the current
     frames s..s+2, then ONE launch runs the denoise segment (3 frames) and the cache-update
