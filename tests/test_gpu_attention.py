@@ -273,6 +273,45 @@ def test_batched_two_phase_step_full_size():
                 "batched B")
 
 
+def test_largest_ring_with_the_window_across_its_end():
+    """The largest ring the library accepts at the full geometry (448 slots: 2.15 GB per K or
+    V ring, just under the attention kernel's 32-bit offset limit), with the window's 21
+    frames 440..460 in slots 440..447 and 0..12: key and value tiles come from the ring's
+    last bytes and across its wrap.  One batched launch (denoise frames 446..460 and the
+    cache-update frame 445, both over 440..460); sampled rows of both against the oracle."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["batched"]
+    N = g.tokens_per_frame
+    slot_bytes = N * g.n_heads * g.head_dim * 2
+    capacity = (0x7FFFFFF0 - 1) // slot_bytes
+    assert capacity == 448
+    assert rf.kvcache_bytes(capacity) == capacity * slot_bytes
+    with pytest.raises(rf.RfError):
+        rf.kvcache_bytes(capacity + 1)
+    t_lo, s = 440, 446
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, capacity)
+    data = {t: (synth.frame(g, cfg, s, t, synth.K), synth.frame(g, cfg, s, t, synth.V), ("noisy", s))
+            for t in range(t_lo, t_lo + g.window)}
+    cache.roll(up(np.concatenate([data[t][0] for t in sorted(data)])),
+               up(np.concatenate([data[t][1] for t in sorted(data)])), t_lo)
+    assert cache.window() == list(range(t_lo, t_lo + g.window))
+    qa = synth.frames(g, cfg, s, s, 15, synth.Q)
+    qb = synth.frame(g, cfg, s, s - 1, synth.Q + synth.CLEAN)
+    oa, ob = _out(g, 15), _out(g, 1)
+    rf.window_attention(ctx, cache, [rf.Segment(up(qa), s, oa, t_lo, g.window),
+                                     rf.Segment(up(qb), s - 1, ob, t_lo, g.window)])
+    torch.cuda.synchronize()
+    rk = RotatedKeys(g)
+    hi = t_lo + g.window
+    _check_rows(g, rk, data, qa, s, oa, t_lo, hi, sample_rows(15 * N, N, extra=64, seed=11),
+                "largest ring A")
+    _check_rows(g, rk, data, qb, s - 1, ob, t_lo, hi, sample_rows(N, N, extra=48, seed=12),
+                "largest ring B")
+    del cache
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_batched_step_full_size_every_row_and_canaries():
     """One full check of the batched step (s = 7): every one of the 23,400 + 1,560 output
     rows x 12 heads against the oracle, with canaries -- rows before and after each output
