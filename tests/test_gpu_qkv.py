@@ -119,6 +119,44 @@ def test_identity_blocks_match_the_roll_bit_exact(geom, calls):
         assert np.array_equal(down(cache.v), down(ref.v)), "V ring differs from the roll's"
 
 
+def _equal_but_zero_sign(a, b):
+    """bf16 tensors equal bit for bit, except that -0 (bits 0x8000) counts as +0."""
+    def canon(t):
+        bits = t.view(torch.int16)
+        return torch.where(bits == -32768, torch.zeros_like(bits), bits)
+    return torch.equal(canon(a), canon(b))
+
+
+def test_identity_blocks_into_the_largest_ring_bit_exact():
+    """Full geometry, the largest ring the library accepts (448 slots, 2.15 GB per K or V
+    ring): 16 frames 440..455 projected into slots 440..447 and 0..7 of an empty ring.
+    With identity weight blocks both rings must equal, bit for bit, those a roll of
+    (x, 2x) writes, and q must be -x (compared on the device).  The 38 M inputs hold a
+    few exact zeros; there the device's sum of one signed-zero product and exact +0
+    products is +0 (IEEE round to nearest), where -x or 2x keep the zero's sign, so +0
+    and -0 count as equal."""
+    g = synth.FULL
+    H, D = g.n_heads, g.head_dim
+    capacity, t0, n = 448, 440, 16
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, capacity)
+    ref = rf.KVCache(ctx, capacity)
+    x = synth.layer_input(g, 14, 0, t0, n)
+    xd = up(x)
+    q = torch.empty((x.shape[0], H, D), dtype=torch.bfloat16, device="cuda")
+    print("identity blocks, 448-slot ring: frames 440..455", flush=True)
+    cache.project(xd, up(_identity_weight(g)), q, t0)
+    xv = xd.view(-1, H, D)
+    ref.roll(xv, (2 * xv.float()).to(torch.bfloat16), t0)
+    torch.cuda.synchronize()
+    assert (cache.first, cache.count) == (ref.first, ref.count) == (t0, n)
+    assert _equal_but_zero_sign(q, -xv), "q != -x"
+    assert _equal_but_zero_sign(cache.k, ref.k), "K ring differs from the roll's"
+    assert _equal_but_zero_sign(cache.v, ref.v), "V ring differs from the roll's"
+    del cache, ref
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("geom", [synth.TINY, synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4)])
 def test_random_weights_tiny(geom):
     g = geom
