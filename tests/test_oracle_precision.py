@@ -63,6 +63,33 @@ def test_rounding_changes_the_result_by_bf16_amounts():
     assert 0 < d.max() <= 2.0 ** -6 * np.abs(ex).max()
 
 
+def test_sparse_case_in_closed_form():
+    """Queries and key 0 use dimension 0 only, everything in frame 0 (where dimension 0,
+    a time-axis pair, is not turned), the other keys are zero and the values one-hot on
+    key 0.  Then every score but key 0's is 0 and, with scale 1, key 0's is
+    s = bf16(a * c) for a query a in dimension 0, c = float32(log2 e); for s < 0 the
+    model's output is bf16(P / (L - 1 + P)) in dimension 0 and 0 elsewhere, with the
+    bf16 weight P = bf16(2^s) and L keys."""
+    N, H, D = T.tokens_per_frame, T.n_heads, T.head_dim
+    rng = np.random.default_rng(85)
+    q = np.zeros((N, H, D))
+    q[:, :, 0] = -rng.uniform(0.05, 5.0, (N, H))
+    k = np.zeros((N, H, D))
+    k[0, :, 0] = 1.0
+    v = np.zeros((N, H, D))
+    v[0, :, 0] = 1.0
+    qb = bf16.f64_to_bits(q)
+    m = precision.attend_rows(qb, 0, bf16.f64_to_bits(k), bf16.f64_to_bits(v), 0, *_args(), scale=1.0)
+    c = float(np.float32(precision.LOG2E))
+    s = bf16.round_f64(bf16.bits_to_f64(qb)[:, :, 0] * c)
+    P = bf16.round_f64(np.exp2(s))
+    want = np.zeros((N, H, D))
+    want[:, :, 0] = bf16.round_f64(P / ((N - 1) + P))
+    assert np.array_equal(m, want)
+    # the weights' rounding shows: unrounded weights would give another output somewhere
+    assert np.any(bf16.round_f64(np.exp2(s) / ((N - 1) + np.exp2(s))) != want[:, :, 0])
+
+
 # The stress test's cache-update rows (tests/test_gpu_attention_stress.py, configuration 31,
 # query frame 5 over context frames 0..20, rows sampled with seed 6).
 STRESS_CFG, STRESS_SEED = 31, 6

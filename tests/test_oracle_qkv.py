@@ -71,6 +71,14 @@ def test_cache_entries_rotate_the_stored_key():
     q, kr, v = qkv.cache_entries(xb, _bits(w), t0, gh, gw, pairs, 10000.0)
     assert not q.any() and not v.any()
     assert np.array_equal(kr, rope3d.rope_spec_bits(xb.reshape(-1, H, D), t0, gh, gw, pairs, 10000.0))
+    # W_k = w3 I with w3 = bf16(1/3) = 0.333984375: each key x * w3 is exact in float64 but
+    # not a bf16 value; the cache holds its bf16 rounding, and the rotated key is the
+    # specification of that stored key (not a rotation of the unrounded product)
+    w3 = 0.333984375
+    q, kr, v = qkv.cache_entries(xb, _bits(w * w3), t0, gh, gw, pairs, 10000.0)
+    stored = _bits(bf16.bits_to_f64(xb) * w3).reshape(-1, H, D)
+    assert not np.array_equal(stored, xb.reshape(-1, H, D))
+    assert np.array_equal(kr, rope3d.rope_spec_bits(stored, t0, gh, gw, pairs, 10000.0))
 
 
 def test_rounding_is_once_from_float64():

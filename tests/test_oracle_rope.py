@@ -186,6 +186,41 @@ def test_spec_bits_against_rational_arithmetic():
         assert got[i, h, 2 * p + 1] == _nearest_bf16_fraction(y1)
 
 
+def test_spec_uses_the_float32_tables():
+    """The specification rotates with float32-rounded cos/sin (the device's tables), not
+    float64 ones.  The two choices round an element to different bf16 values only about
+    once in 2^16 elements, so this pin scans a 3.2 M-element block for every element where
+    they differ and checks the specification there with rational arithmetic."""
+    rng = np.random.default_rng(9)
+    L, H, t0 = 4 * N, 4, 37
+    xb = bf16.f64_to_bits(rng.standard_normal((L, H, D)))
+    x = bf16.bits_to_f64(xb)
+    got = rope3d.rope_spec_bits(xb, t0, GH, GW, PAIRS, BASE)
+    # cos/sin written out here: pair j of an axis with P pairs turns by pos * BASE^(-j/P)
+    i = np.arange(L)
+    axes = [(t0 + i // N, PAIRS[0]), ((i % N) // GW, PAIRS[1]), (i % GW, PAIRS[2])]
+    c64, s64 = [], []
+    for pos, P in axes:
+        table = {int(p): [(math.cos(float(p) * BASE ** (-(j / P))), math.sin(float(p) * BASE ** (-(j / P))))
+                          for j in range(P)] for p in np.unique(pos)}
+        c64.append(np.array([[cs[0] for cs in table[int(p)]] for p in pos]))
+        s64.append(np.array([[cs[1] for cs in table[int(p)]] for p in pos]))
+    c64, s64 = np.concatenate(c64, axis=1)[:, None, :], np.concatenate(s64, axis=1)[:, None, :]
+    c32, s32 = c64.astype(np.float32).astype(np.float64), s64.astype(np.float32).astype(np.float64)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    cand = []
+    for k, (f32_val, f64_val) in enumerate([(x0 * c32 - x1 * s32, x0 * c64 - x1 * s64),
+                                            (x0 * s32 + x1 * c32, x0 * s64 + x1 * c64)]):
+        differ = bf16.f64_to_bits(f32_val) != bf16.f64_to_bits(f64_val)
+        cand += [(a, b, cc, k) for a, b, cc in zip(*np.nonzero(differ))]
+    assert len(cand) >= 10, len(cand)
+    for a, b, p, k in cand:
+        fc, fs = Fraction(float(c32[a, 0, p])), Fraction(float(s32[a, 0, p]))
+        f0, f1 = Fraction(float(x0[a, b, p])), Fraction(float(x1[a, b, p]))
+        exact = f0 * fc - f1 * fs if k == 0 else f0 * fs + f1 * fc
+        assert got[a, b, 2 * p + k] == _nearest_bf16_fraction(Fraction(float(exact)))
+
+
 def test_absolute_frame_index_is_used():
     rng = np.random.default_rng(8)
     x = rng.standard_normal((N, 1, D))
