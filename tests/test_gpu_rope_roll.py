@@ -143,6 +143,32 @@ def test_roll_full_cache_update_bit_exact():
     assert np.array_equal(K2[1:], Kb[1:]) and np.array_equal(V2[1:], Vb[1:])
 
 
+def test_roll_largest_ring_bit_exact():
+    """Full geometry, the largest ring the library accepts (448 slots): 16 frames 440..455
+    rolled into an empty ring land in slots 440..447 and 0..7, bit-exact against the RoPE
+    specification (keys) and the blocked values; a slot between them stays untouched."""
+    g = synth.FULL
+    N = g.tokens_per_frame
+    capacity, t0, n = 448, 440, 16
+    ctx = _ctx(g)
+    cache = rf.KVCache(ctx, capacity)
+    k = synth.frames(g, 3, 0, t0, n, synth.K)
+    v = synth.frames(g, 3, 0, t0, n, synth.V)
+    print("roll 16 frames into slots 440..447, 0..7 of a 448-slot ring", flush=True)
+    cache.roll(up(k), up(v), t0)
+    assert (cache.first, cache.count) == (t0, n)
+    torch.cuda.synchronize()
+    for f in (0, 7, 8, 15):  # slots 440, 447 (the ring's last bytes), 0, 7
+        slot = (t0 + f) % capacity
+        kb = down(cache.k[slot:slot + 1])
+        vb = down(cache.v[slot:slot + 1])
+        assert np.array_equal(ring_frame_k(kb, 0), _spec(g, k[f * N:(f + 1) * N], t0 + f)), slot
+        assert np.array_equal(ring_frame_v(vb, 0), v[f * N:(f + 1) * N]), slot
+    assert not cache.k[100].any() and not cache.v[100].any()
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_roll_strided_inputs_and_errors():
     g = synth.TINY
     W, N, H, D = g.window, g.tokens_per_frame, g.n_heads, g.head_dim
