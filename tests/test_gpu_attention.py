@@ -312,6 +312,52 @@ def test_largest_ring_with_the_window_across_its_end():
     torch.cuda.empty_cache()
 
 
+def test_two_contexts_on_two_streams_at_once():
+    """Two contexts, each with its own ring and workspace, run batched launches (whole and
+    key-split tiles) on two streams at the same time, three each, interleaved; every output
+    equals, bit for bit, what the same launch gives alone: the contexts share no state."""
+    g, cfg = synth.FULL, synth.WORKLOAD_IDS["batched"]
+    N, W = g.tokens_per_frame, g.window
+    s = 9
+    kall = up(synth.frames(g, cfg, s, s - 6, W, synth.K))
+    vall = up(synth.frames(g, cfg, s, s - 6, W, synth.V))
+    ctxs = [_ctx(g), _ctx(g)]
+    caches = []
+    for c in ctxs:
+        cache = rf.KVCache(c, W)
+        cache.roll(kall, vall, s - 6)
+        caches.append(cache)
+    qs = [(up(synth.frames(g, cfg + 100 * i, s, s, 15, synth.Q)),
+           up(synth.frame(g, cfg + 100 * i, s, s - 1, synth.Q + synth.CLEAN))) for i in range(2)]
+
+    def launch(i, oa, ob):
+        rf.window_attention(ctxs[i], caches[i], [rf.Segment(qs[i][0], s, oa, s - 6, W),
+                                                 rf.Segment(qs[i][1], s - 1, ob, s - 6, W)])
+
+    alone = []
+    for i in range(2):
+        oa, ob = _out(g, 15), _out(g, 1)
+        launch(i, oa, ob)
+        torch.cuda.synchronize()
+        alone.append((oa, ob))
+    outs = [[(_out(g, 15), _out(g, 1)) for _ in range(3)] for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    main = torch.cuda.current_stream()
+    for st in streams:
+        st.wait_stream(main)
+    print("two contexts, two streams: 3 + 3 batched launches", flush=True)
+    for r in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                launch(i, *outs[i][r])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(3):
+            for got, want in zip(outs[i][r], alone[i]):
+                assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (i, r)
+    assert not torch.equal(alone[0][0], alone[1][0])  # the two query sets differ
+
+
 def test_batched_step_full_size_every_row_and_canaries():
     """One full check of the batched step (s = 7): every one of the 23,400 + 1,560 output
     rows x 12 heads against the oracle, with canaries -- rows before and after each output
