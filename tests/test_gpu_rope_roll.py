@@ -53,6 +53,64 @@ def test_rope3d_partial_frame_strided_and_in_place():
     assert not fused[:, 0].any() and not fused[:, 2].any()  # neighbours untouched
 
 
+def test_one_context_from_four_threads_and_streams():
+    """One context shared by four host threads, each on a stream of its own (default
+    priority), applying the RoPE and rolling its own ring at once, and one thread's call
+    failing validation meanwhile: every output is bit-exact and each thread's error
+    detail is its own."""
+    import threading
+    g = synth.TINY
+    ctx = _ctx(g)
+    N = g.tokens_per_frame
+    xs = [synth.frames(g, 20 + i, 0, 3 * i, 4, synth.Q) for i in range(4)]
+    kv = [(synth.frames(g, 30 + i, 0, i, 3, synth.K), synth.frames(g, 30 + i, 0, i, 3, synth.V)) for i in range(4)]
+    dev_x = [up(x) for x in xs]
+    dev_kv = [(up(k), up(v)) for k, v in kv]
+    caches = [rf.KVCache(ctx, g.window) for _ in range(4)]
+    ys = [[None] * 5 for _ in range(4)]
+    errs = [None] * 4
+    torch.cuda.synchronize()
+    barrier = threading.Barrier(4)
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                barrier.wait()
+                for r in range(5):
+                    ys[i][r] = ctx.rope3d_apply(dev_x[i], 3 * i)
+                caches[i].roll(dev_kv[i][0], dev_kv[i][1], i)
+                if i == 2:  # a call that fails validation on this thread only
+                    with pytest.raises(rf.RfError, match="roll start"):
+                        caches[i].roll(dev_kv[i][0], dev_kv[i][1], 100)
+                    errs[i] = rf.lib().rf_last_error().decode()
+                else:
+                    errs[i] = rf.lib().rf_last_error().decode()
+                st.synchronize()
+        except BaseException as e:  # reported by the main thread
+            errs[i] = e
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert not isinstance(errs[i], BaseException), errs[i]
+        want = _spec(g, xs[i], 3 * i)
+        for r in range(5):
+            assert np.array_equal(down(ys[i][r]), want), (i, r)
+        Kb, Vb = down(caches[i].k), down(caches[i].v)
+        for f in range(3):
+            slot = (i + f) % g.window
+            assert np.array_equal(ring_frame_k(Kb, slot), _spec(g, kv[i][0][f * N:(f + 1) * N], i + f))
+            assert np.array_equal(ring_frame_v(Vb, slot), kv[i][1][f * N:(f + 1) * N])
+    assert "roll start 100" in errs[2]
+    assert all(errs[i] == "" for i in (0, 1, 3)), errs
+
+
 def test_rope3d_errors():
     g = synth.TINY
     ctx = _ctx(g, max_frame=10)
