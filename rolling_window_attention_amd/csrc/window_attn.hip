@@ -13,13 +13,15 @@
 // ordinary way: one work-group per tile, numbered so that each XCD walks
 // consecutive tiles of one head and its resident work-groups read the same
 // K/V tiles at about the same time (L2 reuse).  The tiles left over for a
-// last, partly filled round are not run one per work-group: their key tiles
-// (64 keys each) are dealt out as equal contiguous ranges to one work-group
-// per slot (stream-K style), so the last round takes only the time its work
-// needs.  A tile cut by a range boundary leaves one partial result
-// (unnormalised O, running max, row sum) per piece in the workspace, and
-// window_attn_fixup merges the pieces.  A launch with fewer tiles than slots
-// (the cache-update pass alone) is split this way entirely.
+// last, partly filled round are not run one per work-group: each is cut into
+// the same n_split equal ranges of its key tiles (64 keys each), one
+// work-group per piece, with n_split chosen on the host so that those pieces
+// end soonest; the pieces are dealt so that the work-groups of one XCD run
+// the same key range of consecutive tiles of one head (L2 reuse again).  Each
+// piece leaves a partial result (unnormalised O, running max, row sum) in the
+// workspace, and window_attn_fixup merges a tile's pieces.  A launch with
+// fewer tiles than slots (the cache-update pass alone) is split this way
+// entirely.
 //
 // Per query tile: eight waves of 32 query rows (two per SIMD) share each K/V
 // tile, which the work-group fetches and stages once (a wave whose rows all lie

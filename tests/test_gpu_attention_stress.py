@@ -10,7 +10,7 @@ split, against the float64 oracle (same tolerances as test_gpu_attention.py).
   rises by more than 8 several times as the kernel walks the context (the lazy rescale of
   O and l with large shifts);
 * eight segments with different context ranges in one launch (the segment lookup of whole
-  tiles, of stream-K pieces and of the merge kernel).
+  tiles, of key-split pieces and of the merge kernel).
 
 Every launch runs the batched layout (a 15-frame and a 1-frame segment over 21 frames,
 1,188 query tiles), so both whole tiles and key-split tiles are produced; rows are sampled
