@@ -259,10 +259,12 @@ typedef struct {
  * recompiled or reallocated when it changes.
  *
  * Work split: query tiles of 256 rows run whole on the GPU's work-group
- * slots (one per CU) in full rounds; the tiles of a last, partly filled round are cut
- * along their keys into equal shares for all slots and merged by a second
- * kernel on the same stream (the result does not depend on the split beyond
- * float32 rounding; it is deterministic for a given launch shape).
+ * slots (one per CU) in full rounds; each tile of a last, partly filled round
+ * is cut into the same number of equal key ranges (chosen so that these pieces
+ * end soonest, at most two pieces per slot), one work-group per piece, and the
+ * pieces are merged by a second kernel on the same stream (the result does not
+ * depend on the split beyond float32 rounding; it is deterministic for a given
+ * launch shape).
  *
  * Errors: RF_ERR_NULL, RF_ERR_ALIGN, RF_ERR_SHAPE (n_segs outside
  * 1..RF_MAX_SEGMENTS, q_tokens/ctx_frames < 1, q_tok0 outside 0..N-1,
@@ -301,9 +303,9 @@ rf_status rf_window_attention_rawk(const rf_ctx* ctx, const rf_kvcache* c,
  * tiles go to a static device array of the library instead of the context's
  * workspace.  No allocation happens in this call.
  *
- * The array holds the partial results of at most 256 split work-groups
- * (2 x 256 x 130 KB = 68 MB; a launch splits over at most one work-group per
- * compute unit, 256 on an MI355X).  Each device keeps its own copy from the
+ * The array holds 512 partial results (2 x 256 x 130 KB = 68 MB): the most a
+ * launch makes on a GPU of up to 256 compute units (256 on an MI355X), whose
+ * split round has at most two pieces per work-group slot.  Each device keeps its own copy from the
  * library's load until the process ends; its address is looked up when the
  * first context of a device is created.  A launch that would need more
  * returns RF_ERR_SHAPE before anything is enqueued; RF_ERR_HIP if the array's

@@ -37,7 +37,8 @@ struct rf_ctx {
 };
 
 // Static attention workspace for rf_window_attention_noalloc: room for the
-// partial results of kScratchWorkers split work-groups (two pieces each), 68 MB.
+// partial results of two pieces per work-group slot of a GPU of up to
+// kScratchWorkers compute units (512 pieces, 68 MB).
 // Each device holds its own copy from the library's load until the process
 // ends.  In host code `scratch` is only a host-side stand-in: its device
 // address comes from hipGetSymbolAddress, per device (scratch_address).
