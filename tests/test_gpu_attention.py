@@ -15,6 +15,7 @@ import torch
 import rolling_window_attention_amd as rf
 from rolling_window_attention_amd import synth
 from oracle import attention as oatt
+from oracle import rope3d as orope
 
 from gpu_util import (RotatedKeys, assert_close, down, f64, oracle_rows, sample_rows, up)
 
@@ -309,6 +310,54 @@ def test_largest_ring_with_the_window_across_its_end():
                 "largest ring B")
     del cache
     gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_largest_segment_the_library_accepts():
+    """One segment of the most query tokens the library accepts, 2^24 - 1 (the device's
+    token -> frame, row, column division is exact below 2^24): 10,755 frames of queries,
+    51.5 GB of Q and as much O, 786,432 query tiles in 3,072 whole rounds, over a 21-frame
+    window.  A segment of 2^24 tokens is refused before any launch.  Sampled rows of the
+    first and last tiles, frame edges far into the segment and random rows against the
+    oracle, each query rotated at its own position."""
+    g = synth.FULL
+    N, H, D, W = g.tokens_per_frame, g.n_heads, g.head_dim, g.window
+    n, q_t0, cfg = (1 << 24) - 1, 5, 61
+    ctx = _ctx(g, max_frame=16384)
+    cache = rf.KVCache(ctx, W)
+    k = synth.frames(g, cfg, 0, 0, W, synth.K)
+    v = synth.frames(g, cfg, 0, 0, W, synth.V)
+    cache.roll(up(k), up(v), 0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg)
+    q_all = torch.randn((n + 1, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    o_all = torch.full((n + 1, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rf.RfError, match="too many query tokens"):
+        rf.window_attention(ctx, cache, [rf.Segment(q_all, q_t0, o_all, 0, W)])
+    q, o = q_all[:n], o_all[:n]
+    print(f"one segment of {n} query tokens over {W * N} keys", flush=True)
+    rf.window_attention(ctx, cache, [rf.Segment(q, q_t0, o, 0, W)])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    last = (n - 1) // 256 * 256
+    rows = {0, 1, 31, 32, 255, 256, last - 1, last, last + 31, last + 32, n - 2, n - 1}
+    for f in rng.integers(1, n // N, 16):
+        rows.update({int(f) * N - 1, int(f) * N})
+    rows.update(int(r) for r in rng.integers(0, n, 48))
+    rows = np.array(sorted(rows))
+    idx = torch.from_numpy(rows).cuda()
+    qb = q.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    got = f64(o.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16))
+    kh = orope.rope_exact(f64(k), 0, g.grid_h, g.grid_w, g.pairs, g.base)
+    vf = f64(v)
+    want = np.empty((len(rows), H, D))
+    for j, i in enumerate(rows):
+        qh = orope.rope_exact(f64(qb[j:j + 1]), q_t0 + int(i) // N, g.grid_h, g.grid_w, g.pairs,
+                                    g.base, tok0=int(i) % N)[0]
+        for h in range(H):
+            want[j, h] = oatt.attend_head(qh[None, h], kh[:, h], vf[:, h], 1.0 / np.sqrt(D))[0]
+    assert_close(got, want, "largest segment")
+    del q_all, o_all, q, o, cache
     torch.cuda.empty_cache()
 
 
