@@ -227,6 +227,65 @@ def test_roll_largest_ring_bit_exact():
     torch.cuda.empty_cache()
 
 
+def test_roll_of_a_whole_largest_ring():
+    """The largest roll: 448 frames (the whole largest accepted ring, 4.3 GB of K and V) in
+    one call into an empty ring, starting at frame 900 (slot 4, so it wraps); sampled
+    frames bit-exact, among them those in the ring's last and first slots."""
+    g = synth.FULL
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    capacity, t0 = 448, 900
+    ctx = _ctx(g, max_frame=2048)
+    cache = rf.KVCache(ctx, capacity)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    k = torch.randn((capacity * N, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((capacity * N, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    print("roll 448 frames into a 448-slot ring", flush=True)
+    cache.roll(k, v, t0)
+    assert (cache.first, cache.count) == (t0, capacity)
+    torch.cuda.synchronize()
+    for f in (0, capacity - 1 - t0 % capacity, capacity - t0 % capacity, 200, capacity - 1):
+        slot = (t0 + f) % capacity
+        kf, vf = down(k[f * N:(f + 1) * N]), down(v[f * N:(f + 1) * N])
+        assert np.array_equal(ring_frame_k(down(cache.k[slot:slot + 1]), 0), _spec(g, kf, t0 + f)), slot
+        assert np.array_equal(ring_frame_v(down(cache.v[slot:slot + 1]), 0), vf), slot
+    del cache, k, v
+    torch.cuda.empty_cache()
+
+
+def test_rope3d_longest_block_in_place():
+    """rf_rope3d_apply on the most tokens the device index math allows (2^24 - 1: 51.5 GB,
+    10,755 frames), in place; sampled tokens -- the first and last, frame edges far into
+    the block, random ones -- bit-exact against the specification at their own
+    positions."""
+    g = synth.FULL
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    n, t0 = (1 << 24) - 1, 3
+    ctx = _ctx(g, max_frame=16384)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    x = torch.randn((n, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    rng = np.random.default_rng(8)
+    rows = {0, 1, N - 1, N, n - 2, n - 1}
+    for f in rng.integers(1, n // N, 12):
+        rows.update({int(f) * N - 1, int(f) * N})
+    rows.update(int(r) for r in rng.integers(0, n, 32))
+    rows = np.array(sorted(rows))
+    idx = torch.from_numpy(rows).cuda()
+    before = x.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    print(f"rope3d in place on {n} tokens", flush=True)
+    ctx.rope3d_apply(x, t0, y=x)
+    torch.cuda.synchronize()
+    after = x.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    for j, i in enumerate(rows):
+        frame = np.zeros((N, H, D), np.uint16)  # the sampled token at its place in its frame
+        frame[i % N] = before[j]
+        want = _spec(g, frame, t0 + int(i) // N)[i % N]
+        assert np.array_equal(after[j], want), int(i)
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_roll_strided_inputs_and_errors():
     g = synth.TINY
     W, N, H, D = g.window, g.tokens_per_frame, g.n_heads, g.head_dim
