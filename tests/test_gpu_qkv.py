@@ -157,6 +157,33 @@ def test_identity_blocks_into_the_largest_ring_bit_exact():
     torch.cuda.empty_cache()
 
 
+def test_identity_projection_of_a_whole_largest_ring():
+    """The largest projection call: 448 frames (698,880 tokens, 2,730 token tiles) filling
+    an empty 448-slot ring from frame 900 (slot 4, so it wraps), identity weight blocks;
+    both rings and q against a roll of (x, 2x) and -x, on the device, +0 and -0 equal."""
+    g = synth.FULL
+    N, H, D = g.tokens_per_frame, g.n_heads, g.head_dim
+    capacity, t0 = 448, 900
+    ctx = rf.Context(g.grid_h, g.grid_w, H, D, g.pairs, g.base, 2048)
+    cache = rf.KVCache(ctx, capacity)
+    ref = rf.KVCache(ctx, capacity)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(15)
+    xd = torch.randn((capacity * N, H * D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    q = torch.empty((capacity * N, H, D), dtype=torch.bfloat16, device="cuda")
+    print("identity blocks, 448 frames into a 448-slot ring", flush=True)
+    cache.project(xd, up(_identity_weight(g)), q, t0)
+    xv = xd.view(-1, H, D)
+    ref.roll(xv, (2 * xv.float()).to(torch.bfloat16), t0)
+    torch.cuda.synchronize()
+    assert (cache.first, cache.count) == (ref.first, ref.count) == (t0, capacity)
+    assert _equal_but_zero_sign(q, -xv), "q != -x"
+    assert _equal_but_zero_sign(cache.k, ref.k), "K ring differs from the roll's"
+    assert _equal_but_zero_sign(cache.v, ref.v), "V ring differs from the roll's"
+    del cache, ref, xd, q
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("geom", [synth.TINY, synth.Geometry(grid_h=4, grid_w=6, n_heads=3, window=4)])
 def test_random_weights_tiny(geom):
     g = geom
