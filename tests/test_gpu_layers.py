@@ -114,6 +114,39 @@ def test_grouped_roll_full_size_cache_update(L):
         assert not bool(c.k[1:].view(torch.int16).any()) and not bool(c.v[1:].view(torch.int16).any())
 
 
+def test_grouped_roll_of_the_most_layers():
+    """The most layers one grouped roll accepts, 65,535 (the grid's y extent), on the tiny
+    grid with 2-slot rings (39 GB in all) and the same frames for every layer (layer
+    stride 0): two frames, then a third that evicts the first.  Sampled layers' rings
+    bit-exact, every layer's device window advanced, 65,536 layers refused."""
+    g = synth.TINY
+    N = g.tokens_per_frame
+    L, W = 65535, 2
+    ctx = _ctx(g)
+    caches = [rf.KVCache(ctx, W) for _ in range(L)]
+    rings = rf.DeviceRings(caches)
+    model = RingModel(W)
+    for step, (t0, n) in enumerate([(0, 2), (2, 1)]):
+        k = synth.frames(g, 52, step, t0, n, synth.K)
+        v = synth.frames(g, 52, step, t0, n, synth.V)
+        kd, vd = up(k), up(v)
+        print(f"{L} layers: roll frames {t0}..{t0 + n - 1}", flush=True)
+        rings.roll(kd.unsqueeze(0).expand(L, *kd.shape), vd.unsqueeze(0).expand(L, *vd.shape), t0)
+        model.roll(t0, n, [(k[i * N:(i + 1) * N], v[i * N:(i + 1) * N], t0 + i) for i in range(n)])
+    torch.cuda.synchronize()
+    assert all((c.first, c.count) == (1, 2) for c in caches)
+    assert _dev_windows(rings) == [(1, 2)] * L
+    K, V = _expected_ring(g, model, W)
+    for l in (0, 1, 255, 256, 32767, L - 2, L - 1):
+        assert np.array_equal(down(caches[l].k), K), l
+        assert np.array_equal(down(caches[l].v), V), l
+    with pytest.raises(rf.RfError):
+        rf.DeviceRings(caches + [rf.KVCache(ctx, W)])
+    del rings, caches
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_grouped_roll_matches_separate_rolls_and_validates():
     """One grouped launch leaves the same bits as L separate rf_kvcache_roll calls (shared
     input with layer stride 0 included); illegal rolls are refused for the group before
